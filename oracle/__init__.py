@@ -1,0 +1,16 @@
+"""fp64 CPU oracle for exact softmax attention.
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import anything from this package.
+It never imports the HIP library package (``exact_io_aware_27_amd``) and the
+library never imports it; the two share no code.
+
+- ``attention``: the plain definition, O = softmax(scale*QK^T)V and
+  LSE = m + ln(l), in C (``attn_oracle.c``), fp64, threaded over row blocks.
+- ``online``: the pages' tiled recurrence (running max m and running sum l)
+  and the two-block merge identity, in NumPy fp64, used to pin the reading
+  of the recurrence against the definition.
+"""
+
+from .oracle import attention, build, library_path  # noqa: F401
+from .online import merge_partials, online_attention  # noqa: F401

@@ -1,0 +1,120 @@
+"""ctypes front end of the fp64 C oracle (``attn_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  Parity of the C code
+is pinned in tests/test_oracle.py: closed forms, PyTorch's CPU
+``scaled_dot_product_attention`` in float64, and the two-block merge identity
+of "FlashAttention evolution" (letsgetai.github.io), section on the core
+mechanism, merge equation.
+"""
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "attn_oracle.c")
+_LIB = os.path.join(_HERE, "libattn_oracle.so")
+_lib = None
+
+ORACLE_STATUS = {0: "OK", 1: "BAD_ARG", 2: "NO_MEMORY", 3: "PSUM"}
+
+
+def library_path():
+    return _LIB
+
+
+def build(force=True):
+    """Compile attn_oracle.c with gcc into oracle/libattn_oracle.so.
+
+    Plain -O2, no -ffast-math and no -march, so fp64 arithmetic keeps its
+    IEEE meaning and the library runs on any x86-64 host.
+    """
+    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+        return _LIB
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+           "-fno-fast-math", "-ffp-contract=off", "-Wall", "-Wextra",
+           "-o", tmp, _SRC, "-lm"]
+    subprocess.check_call(cmd)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def load_library(path):
+    """Open a compiled oracle library and declare oracle_attn's signature."""
+    lib = ctypes.CDLL(path)
+    f = lib.oracle_attn
+    f.restype = ctypes.c_int
+    p = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    f.argtypes = [p, p, p, i64, i64, i64, ctypes.c_int, ctypes.c_double,
+                  p, i64, p, p, p, ctypes.c_int]
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build(force=False)
+        _lib = load_library(_LIB)
+    return _lib
+
+
+def default_threads():
+    n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
+
+
+def _bf16_bits(x):
+    """bf16 bit patterns as a contiguous uint16 array (torch bf16 tensor or uint16 array)."""
+    if isinstance(x, np.ndarray):
+        if x.dtype != np.uint16:
+            raise TypeError("numpy input must hold bf16 bit patterns as uint16")
+        return np.ascontiguousarray(x)
+    import torch  # only for the bf16 -> bits view of a CPU tensor
+
+    if x.dtype != torch.bfloat16:
+        raise TypeError("torch input must be bfloat16")
+    return np.ascontiguousarray(x.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16))
+
+
+def attention(q, k, v, causal, scale, rows=None, nthreads=None, return_psum_dev=False, lib=None):
+    """Exact attention in fp64 for bf16 inputs of shape [B, H, N, d].
+
+    rows: None for every query row, else an int array [B*H, R] (or [B, H, R])
+    of query indices per (batch, head).
+    Returns (o, lse): o float64 [B, H, R, d], lse float64 [B, H, R]
+    (and psum_dev float64 [B, H, R], |sum_j P_ij - 1|, if asked).
+    lib: a library from load_library() to use instead of the built one.
+    """
+    qb, kb, vb = _bf16_bits(q), _bf16_bits(k), _bf16_bits(v)
+    if qb.ndim != 4 or qb.shape != kb.shape or qb.shape != vb.shape:
+        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    B, H, N, d = qb.shape
+    BH = B * H
+    if rows is None:
+        R = N
+        rows_arr = None
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(BH, -1))
+        R = rows_arr.shape[1]
+    o = np.empty((BH, R, d), dtype=np.float64)
+    lse = np.empty((BH, R), dtype=np.float64)
+    dev = np.empty((BH, R), dtype=np.float64)
+    lib = lib or _load()
+    st = lib.oracle_attn(qb.ctypes.data, kb.ctypes.data, vb.ctypes.data, BH, N, d,
+                         1 if causal else 0, float(scale),
+                         None if rows_arr is None else rows_arr.ctypes.data, R,
+                         o.ctypes.data, lse.ctypes.data, dev.ctypes.data,
+                         int(nthreads or default_threads()))
+    if st != 0:
+        raise RuntimeError("oracle_attn failed: %s" % ORACLE_STATUS.get(st, st))
+    out = (o.reshape(B, H, R, d), lse.reshape(B, H, R))
+    if return_psum_dev:
+        out = out + (dev.reshape(B, H, R),)
+    return out
