@@ -1,0 +1,123 @@
+"""Thin ctypes binding of libattn.so (include/attn.h).
+
+Argument marshalling only: tensors become device pointers, the stream
+becomes a hipStream_t handle, and a nonzero status becomes an exception.
+Every step of the computation runs in the library's HIP kernels; there is no
+fallback.  If the library is missing, loading raises.
+
+torch is imported before the library is opened so that libattn.so binds to
+the HIP runtime torch already loaded (both carry the soname
+libamdhip64.so.7): one runtime per process, so torch's streams and device
+pointers are valid in the library.
+"""
+
+import ctypes
+import os
+
+import torch  # noqa: F401  (must be loaded first: see the module docstring)
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+
+ATTN_OK = 0
+STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_NULL_PTR", 2: "ATTN_BAD_SHAPE", 3: "ATTN_UNSUPPORTED_D",
+                4: "ATTN_BAD_SCALE", 5: "ATTN_MISALIGNED", 6: "ATTN_ALIAS", 7: "ATTN_HIP"}
+EXPORTS = ("attn_fwd", "attn_status_string", "attn_last_hip_error")
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status, hip_error=0):
+        self.status = status
+        self.hip_error = hip_error
+        msg = STATUS_NAMES.get(status, str(status))
+        if hip_error:
+            msg += " (hipError %d)" % hip_error
+        super().__init__(msg)
+
+
+def load():
+    """Open libattn.so and declare its signatures; raise if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise FileNotFoundError(
+            "libattn.so is not built (%s); run __graft_entry__.build() or "
+            "python exact_io_aware_27_amd/build.py" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    p, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_fwd.argtypes = [p, p, p, p, p, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float, p]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_status_string.argtypes = [ctypes.c_int]
+    lib.attn_last_hip_error.restype = ctypes.c_int
+    lib.attn_last_hip_error.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream  # torch.cuda.Stream
+
+
+def _check(x, name, shape, dtype):
+    """Tensors handed to the kernel must be exactly what its grid assumes."""
+    if x is None or isinstance(x, int):
+        return
+    if x.dtype != dtype or tuple(x.shape) != shape or not x.is_contiguous() or not x.is_cuda:
+        raise ValueError("%s must be a contiguous %s CUDA tensor of shape %s, got %s %s %s"
+                         % (name, dtype, shape, x.dtype, tuple(x.shape), x.device))
+
+
+def attn_fwd_status(q, k, v, o, lse, B, H, N, d, causal, scale, stream=None):
+    """Call attn_fwd and return its status code (0 = ATTN_OK).
+
+    q, k, v, o: device tensors (or raw pointers) bf16 [B, H, N, d];
+    lse: fp32 [B, H, N] device tensor, pointer, or None;
+    stream: torch.cuda.Stream, a raw hipStream_t, or None (null stream).
+    Tensors are checked against (B, H, N, d); raw pointers are the caller's
+    responsibility.
+    """
+    shape = (int(B), int(H), int(N), int(d))
+    for x, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _check(x, name, shape, torch.bfloat16)
+    _check(lse, "lse", shape[:3], torch.float32)
+    lib = load()
+    return lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(N),
+                        int(d), 1 if causal else 0, float(scale), _stream(stream))
+
+
+def attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, stream=None):
+    """attn_fwd of include/attn.h; raises AttnError on a nonzero status."""
+    st = attn_fwd_status(q, k, v, o, lse, B, H, N, d, causal, scale, stream)
+    if st != ATTN_OK:
+        raise AttnError(st, load().attn_last_hip_error() if st == 7 else 0)
+
+
+def attention(q, k, v, causal=False, scale=None, with_lse=True, stream=None):
+    """Allocate O (and LSE) like q and run attn_fwd on torch's current stream.
+
+    q, k, v: contiguous bf16 CUDA tensors [B, H, N, d].  Returns (o, lse).
+    """
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = d ** -0.5
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if with_lse else None
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, stream)
+    return o, lse

@@ -1,0 +1,99 @@
+/*
+ * attn.h -- C ABI of libattn.so: exact, fused attention forward pass on
+ * AMD MI355X (gfx950).
+ *
+ * What the call computes, for every batch b and head h:
+ *
+ *   O   = softmax(scale * Q K^T) V                 (bf16 out, fp32 arithmetic)
+ *   LSE = ln( sum_j exp(scale * q_i . k_j) )       (fp32 out, one per query row)
+ *
+ * This is the attention equation of "FlashAttention evolution"
+ * (letsgetai.github.io), section on why attention is slow, with the scale an
+ * explicit argument (that equation uses 1/sqrt(d)).  The result is reached
+ * with the tiled online softmax of the same page's core-mechanism section
+ * (running max m and running sum l, merged block by block with the two-block
+ * merge equation, divided by l once at the end) and with the FlashAttention-2
+ * loop order and sequence parallelism of "FlashAttention 1-4 evolution cheat
+ * sheet" (argus-lessons), FlashAttention-2 section.  The N x N score and
+ * probability matrices never leave the chip.  Results equal the definition up
+ * to floating-point accumulation order, not bit for bit (the numerical
+ * equivalence paragraph of the "FlashAttention" concept page,
+ * compassingai.com, section 3).
+ *
+ * LSE is the natural-log logsumexp of the scaled, masked logits, i.e. the
+ * saved softmax statistics m + ln(l) that a recomputing backward pass needs
+ * ("FlashAttention evolution", recomputation paragraph).
+ *
+ * Causal mask: key j is visible to query i iff j <= i.  Masked logits take no
+ * part in the max, the sum or the output.
+ */
+#ifndef EXACT_IO_AWARE_ATTN_H
+#define EXACT_IO_AWARE_ATTN_H
+
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define ATTN_API __attribute__((visibility("default")))
+#else
+#define ATTN_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by attn_fwd(). */
+enum attn_status {
+    ATTN_OK = 0,
+    ATTN_NULL_PTR = 1,      /* q, k, v or o is NULL (and the problem is not empty) */
+    ATTN_BAD_SHAPE = 2,     /* B, H or N negative; N * d >= 2^31; a byte size or the
+                               workgroup count overflows */
+    ATTN_UNSUPPORTED_D = 3, /* d is neither 64 nor 128 */
+    ATTN_BAD_SCALE = 4,     /* scale is NaN or infinite */
+    ATTN_MISALIGNED = 5,    /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
+    ATTN_ALIAS = 6,         /* o or lse overlaps q, k or v, or o overlaps lse */
+    ATTN_HIP = 7            /* the kernel launch failed; see attn_last_hip_error() */
+};
+
+/*
+ * attn_fwd -- O = softmax(scale * Q K^T) V and LSE, for all B*H heads.
+ *
+ * q, k, v  device pointers, bf16, contiguous [B][H][N][d] (d fastest).
+ * o        device pointer, bf16, contiguous [B][H][N][d]; fully overwritten.
+ * lse      device pointer, fp32, contiguous [B][H][N], natural log; fully
+ *          overwritten.  NULL: LSE is not written.
+ * B, H, N  batch, heads, sequence length (queries == keys == N).  Any of them
+ *          0 makes the call an immediate no-op returning ATTN_OK.  N need not
+ *          be a multiple of any tile size.
+ * d        head dimension: 64 or 128.
+ * causal   0: every key visible;  nonzero: key j visible to query i iff j <= i.
+ * scale    multiplies q . k before the softmax (usually 1/sqrt(d)); finite.
+ * stream   a hipStream_t passed as void*; NULL is the null (default) stream.
+ *
+ * Ownership: the caller owns every buffer.  The library allocates no device
+ * or host memory, keeps no state between calls and is reentrant; calls on
+ * different streams may run concurrently.
+ * Asynchrony: the call enqueues one kernel on `stream` and returns without
+ * synchronising.  Faults inside the kernel surface at the caller's next
+ * synchronisation, not here.
+ * Errors: arguments are checked in this order, before any HIP runtime call,
+ * so every code but ATTN_HIP is returned without touching a GPU:
+ * BAD_SHAPE, UNSUPPORTED_D, BAD_SCALE, (empty -> OK), NULL_PTR, MISALIGNED,
+ * ALIAS.  No C++ exception crosses this interface.
+ */
+ATTN_API int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+             int64_t B, int64_t H, int64_t N, int64_t d, int causal,
+             float scale, void *stream);
+
+/* Static, human-readable name of a status code ("ATTN_OK", ...). */
+ATTN_API const char *attn_status_string(int status);
+
+/* The hipError_t of the last attn_fwd() call on this thread that returned
+ * ATTN_HIP (0 if none has). */
+ATTN_API int attn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_IO_AWARE_ATTN_H */

@@ -1,0 +1,119 @@
+"""The C ABI without a GPU: the library loads, exports what include/attn.h
+declares, and rejects every bad argument before any HIP runtime call."""
+
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from exact_io_aware_27_amd import attn
+    if not os.path.exists(attn.LIB_PATH):
+        from exact_io_aware_27_amd import build
+        build.build()
+    return attn.load()
+
+
+def _declared():
+    with open(HEADER) as f:
+        text = f.read()
+    return re.findall(r"ATTN_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def test_header_declares_the_abi():
+    assert set(_declared()) == {"attn_fwd", "attn_status_string", "attn_last_hip_error"}
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from exact_io_aware_27_amd import attn
+    out = subprocess.check_output(["nm", "-D", "--defined-only", attn.LIB_PATH], text=True)
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in _declared():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_status_strings(lib):
+    names = ["ATTN_OK", "ATTN_NULL_PTR", "ATTN_BAD_SHAPE", "ATTN_UNSUPPORTED_D",
+             "ATTN_BAD_SCALE", "ATTN_MISALIGNED", "ATTN_ALIAS", "ATTN_HIP"]
+    for code, name in enumerate(names):
+        assert lib.attn_status_string(code).decode() == name
+    assert lib.attn_status_string(99).decode() == "ATTN_UNKNOWN_STATUS"
+    assert lib.attn_last_hip_error() == 0
+
+
+# Fake, never-dereferenced device addresses: validation fails before any use.
+Q, K, V, O, L = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+
+
+def _call(lib, q=Q, k=K, v=V, o=O, lse=L, B=2, H=3, N=100, d=128, causal=1, scale=0.1):
+    return lib.attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), 2), (dict(H=-5), 2), (dict(N=-1), 2),
+    (dict(B=1 << 40, H=1 << 30), 2),              # B*H*N overflows int64
+    (dict(N=1 << 24, d=128), 2),                  # N*d = 2^31
+    (dict(d=96), 3), (dict(d=256), 3), (dict(d=0), 3),
+    (dict(scale=float("nan")), 4), (dict(scale=float("inf")), 4), (dict(scale=-math.inf), 4),
+    (dict(B=0, q=None, k=None, v=None, o=None), 0), (dict(N=0), 0), (dict(H=0), 0),
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(o=None), 1),
+    (dict(q=Q + 8), 5), (dict(o=O + 2), 5), (dict(lse=L + 2), 5),
+    (dict(o=Q + 64), 6), (dict(o=K), 6), (dict(lse=V + 16), 6), (dict(lse=O + 1024), 6),
+    (dict(d=64, scale=float("nan")), 4), (dict(d=7, B=-1), 2),
+])
+def test_argument_errors_before_any_hip_call(lib, kw, status):
+    assert _call(lib, **kw) == status
+
+
+def test_lse_null_is_allowed_past_validation_order(lib):
+    # With lse NULL the only remaining problem is the alias of o and q.
+    assert _call(lib, lse=None, o=Q) == 6
+
+
+def test_q_k_v_may_alias_each_other(lib):
+    # Shared inputs are legal; the only error left is the misaligned output.
+    assert _call(lib, k=Q, v=Q, o=O + 4) == 5
+
+
+def test_binding_rejects_mismatched_tensors():
+    import torch
+    from exact_io_aware_27_amd import attn
+    x = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        attn.attn_fwd_status(x, x, x, x, None, 1, 2, 8, 128, False, 0.1)
+    with pytest.raises(ValueError):
+        attn.attn_fwd_status(x.float(), x, x, x, None, 1, 2, 8, 64, False, 0.1)
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    from exact_io_aware_27_amd import attn
+    monkeypatch.setattr(attn, "_lib", None)
+    monkeypatch.setattr(attn, "LIB_PATH", "/nonexistent/libattn.so")
+    with pytest.raises(FileNotFoundError):
+        attn.load()
+
+
+def test_product_and_oracle_share_no_code():
+    """Neither side imports, includes or links the other."""
+    pkg = os.path.join(ROOT, "exact_io_aware_27_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
+                assert "attn_oracle" not in text, f
+    for f in os.listdir(os.path.join(ROOT, "oracle")):
+        if f.endswith((".py", ".c", ".h")):
+            text = open(os.path.join(ROOT, "oracle", f)).read()
+            assert not re.search(r"^\s*(import|from)\s+exact_io_aware_27_amd", text, re.M), f
+            includes = re.findall(r"^\s*#\s*include\s*[<\"]([^>\"]+)", text, re.M)
+            assert not any("attn.h" in i or "csrc" in i or "attn_launch" in i for i in includes), f

@@ -1,0 +1,229 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle, on a GPU.
+
+Every input is seeded and synthetic (exact_io_aware_27_amd.inputs); every
+expected value comes from the oracle or from a closed form.  Workloads that
+the oracle cannot finish in seconds in full are checked on seeded row
+subsets that always include rows 0 and N-1, in the same launch the bench
+times (the whole problem runs on the GPU; only the comparison is sampled).
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import online
+from exact_io_aware_27_amd import inputs
+import golden_cases
+import parity
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def run(q, k, v, causal, scale, with_lse=True, stream=None):
+    from exact_io_aware_27_amd import attn
+    qd, kd, vd = (x.to(DEV).contiguous() for x in (q, k, v))
+    o, lse = attn.attention(qd, kd, vd, causal=causal, scale=scale, with_lse=with_lse, stream=stream)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def check_full(q, k, v, causal, scale, what):
+    say("case:", what, tuple(q.shape), "causal" if causal else "non-causal")
+    o, lse = run(q, k, v, causal, scale)
+    o_ref, lse_ref = oracle.attention(q, k, v, causal, scale)
+    rep = parity.compare(o, lse, o_ref, lse_ref)
+    say("  ", rep)
+    parity.assert_parity(rep, what)
+    return o, lse
+
+
+@pytest.mark.parametrize("case", golden_cases.load(), ids=lambda c: c["name"])
+def test_golden_closed_forms(case):
+    say("case: golden", case["name"])
+    o, lse = run(case["q"], case["k"], case["v"], case["causal"], case["scale"])
+    rep = parity.compare(o, lse, case["o"][None, None], case["lse"][None, None])
+    say("  ", rep)
+    parity.assert_parity(rep, case["name"])
+
+
+def test_workload_tiny_all_rows():
+    w = inputs.WORKLOADS[0]
+    q, k, v = inputs.workload_qkv(w)
+    check_full(q, k, v, w.causal, w.scale, w.describe())
+
+
+def test_workload_gpt2_small_all_rows():
+    w = inputs.WORKLOADS[1]
+    q, k, v = inputs.workload_qkv(w)
+    check_full(q, k, v, w.causal, w.scale, w.describe())
+
+
+def _sampled(w, R, extra_rows=()):
+    say("case:", w.describe(), "rows/head", R)
+    q, k, v = inputs.workload_qkv(w)
+    o, lse = run(q, k, v, w.causal, w.scale)
+    force = (0, w.N - 1) + tuple(extra_rows)
+    rows = torch.stack([inputs.row_subset(w.N, R, w.seed, bh, force) for bh in range(w.B * w.H)])
+    o_ref, lse_ref = oracle.attention(q, k, v, w.causal, w.scale, rows=rows)
+    rep = parity.compare(parity.gather_rows(o, rows), parity.gather_rows(lse, rows), o_ref, lse_ref)
+    say("  ", rep)
+    parity.assert_parity(rep, w.describe())
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+def test_workload_long_causal_sampled():
+    # Tile boundaries of the 128-row query tiles and 64-key tiles are always in.
+    _sampled(inputs.WORKLOADS[2], 240, extra_rows=(63, 64, 127, 128, 129, 4095, 4096, 8190))
+
+
+def test_workload_large_logits_sampled():
+    w = inputs.WORKLOADS[3]
+    _sampled(w, w.rows_checked)
+
+
+def test_workload_very_long_causal_sampled():
+    w = inputs.WORKLOADS[4]
+    _sampled(w, w.rows_checked)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 2, 31, 63, 64, 65, 127, 128, 129, 200, 1000, 1025])
+def test_ragged_lengths(N, d, causal):
+    q, k, v = inputs.make_qkv(1, 3, N, d, seed=1000 + N + d + causal)
+    check_full(q, k, v, causal, 1.0 / math.sqrt(d), "ragged N=%d d=%d" % (N, d))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_many_heads_and_batches(d):
+    q, k, v = inputs.make_qkv(3, 5, 300, d, seed=77)
+    check_full(q, k, v, True, 1.0 / math.sqrt(d), "B=3 H=5 N=300")
+
+
+def test_scale_argument_is_used():
+    q, k, v = inputs.make_qkv(1, 2, 257, 128, seed=78)
+    check_full(q, k, v, False, 0.37, "scale 0.37")
+    check_full(q, k, v, True, 0.01, "scale 0.01")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_causal_row_zero_is_exactly_v0(d):
+    q, k, v = inputs.make_qkv(2, 2, 500, d, seed=79)
+    o, lse = run(q, k, v, True, 1.0 / math.sqrt(d))
+    assert torch.equal(o[:, :, 0].cpu(), v[:, :, 0])
+    dots = (q[:, :, 0].double() * k[:, :, 0].double()).sum(-1) / math.sqrt(d)
+    assert (lse[:, :, 0].double().cpu() - dots).abs().max().item() <= 1e-4
+
+
+def test_equal_keys_give_mean_of_values():
+    N, d = 700, 128
+    q, _, v = inputs.make_qkv(1, 2, N, d, seed=80)
+    krow = inputs.make_qkv(1, 2, 1, d, seed=81)[1]
+    k = krow.expand(1, 2, N, d).contiguous()
+    for causal in (False, True):
+        o, lse = run(q, k, v, causal, 1.0 / math.sqrt(d))
+        n = torch.arange(1, N + 1, dtype=torch.float64) if causal else torch.full((N,), float(N))
+        vv = v.double()
+        mean = (vv.cumsum(2) / n[None, None, :, None]) if causal else vv.mean(2, keepdim=True).expand_as(vv)
+        s = (q.double() * krow.double()).sum(-1) / math.sqrt(d)
+        rep = parity.compare(o, lse, mean.numpy(), (s + torch.log(n)).numpy())
+        say("  equal keys", causal, rep)
+        parity.assert_parity(rep, "equal keys")
+
+
+def test_one_hot_dominant_logits_select_value_row():
+    N, d = 512, 128
+    _, k, v = inputs.make_qkv(1, 1, N, d, seed=82)
+    perm = torch.randperm(N, generator=torch.Generator().manual_seed(83))
+    q = (k[0, 0, perm] * 16).reshape(1, 1, N, d)
+    o, _ = run(q, k, v, False, 1.0 / math.sqrt(d))
+    s = (q.double()[0, 0] @ k.double()[0, 0].T) / math.sqrt(d)
+    top2 = torch.topk(s, 2, dim=1).values
+    assert (top2[:, 0] - top2[:, 1]).min().item() >= 40
+    assert torch.equal(o[0, 0].cpu(), v[0, 0, perm])
+
+
+def test_split_kv_merge_recovers_full_attention():
+    """Partials over key halves, merged with the merge equation, match the full run.
+
+    This checks that the kernel's LSE is the natural-log logsumexp of the
+    scaled logits over the keys it saw.
+    """
+    N, d = 512, 128
+    h = N // 2
+    q, k, v = inputs.make_qkv(1, 4, N, d, seed=84, sigma_qk=2.0)
+    scale = 1.0 / math.sqrt(d)
+    o_full, lse_full = run(q, k, v, False, scale)
+    for qs in (slice(0, h), slice(h, N)):
+        parts = []
+        for ks in (slice(0, h), slice(h, N)):
+            o_p, l_p = run(q[:, :, qs].contiguous(), k[:, :, ks].contiguous(), v[:, :, ks].contiguous(),
+                           False, scale)
+            parts.append((o_p.double().cpu().numpy(), l_p.double().cpu().numpy()))
+        om, lm = online.merge_partials(parts[0][0], parts[0][1], parts[1][0], parts[1][1])
+        o_ref, l_ref = oracle.attention(q, k, v, False, scale, rows=np.tile(np.arange(N)[qs], (4, 1)))
+        # merged bf16 partials carry one extra bf16 rounding each: compare on the same bar
+        rep = parity.compare(torch.from_numpy(om).to(torch.bfloat16), torch.from_numpy(lm), o_ref, l_ref)
+        say("  merged", rep)
+        parity.assert_parity(rep, "split-kv merge")
+        assert np.abs(lm - lse_full[:, :, qs].double().cpu().numpy()).max() <= 1e-4
+
+
+def test_lse_null_gives_identical_output():
+    q, k, v = inputs.make_qkv(2, 3, 333, 128, seed=85)
+    o1, _ = run(q, k, v, True, 0.1)
+    o2, l2 = run(q, k, v, True, 0.1, with_lse=False)
+    assert l2 is None and torch.equal(o1, o2)
+
+
+def test_runs_are_bitwise_deterministic():
+    q, k, v = inputs.make_qkv(2, 4, 1111, 128, seed=86)
+    a = run(q, k, v, True, 0.088)
+    b = run(q, k, v, True, 0.088)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_every_output_element_is_written():
+    from exact_io_aware_27_amd import attn
+    B, H, N, d = 2, 3, 777, 64
+    q, k, v = (x.to(DEV) for x in inputs.make_qkv(B, H, N, d, seed=87))
+    o = torch.full((B, H, N, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device=DEV)
+    attn.attn_fwd(q, k, v, o, lse, B, H, N, d, True, 0.125, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+def test_non_default_stream_and_no_device_allocation():
+    from exact_io_aware_27_amd import attn
+    B, H, N, d = 1, 4, 1500, 128
+    q, k, v = (x.to(DEV) for x in inputs.make_qkv(B, H, N, d, seed=88))
+    o1 = torch.empty_like(q)
+    o2 = torch.empty_like(q)
+    attn.attn_fwd(q, k, v, o1, None, B, H, N, d, True, 0.09, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()  # default priority
+    before = torch.cuda.memory_allocated()
+    with torch.cuda.stream(s):
+        attn.attn_fwd(q, k, v, o2, None, B, H, N, d, True, 0.09, s)
+    s.synchronize()
+    assert torch.cuda.memory_allocated() == before
+    assert torch.equal(o1, o2)
+
+
+def test_one_hip_runtime_in_process():
+    from exact_io_aware_27_amd import attn
+    attn.load()
+    with open("/proc/self/maps") as f:
+        paths = {line.split()[-1] for line in f if "libamdhip64" in line}
+    assert len(paths) == 1, paths
