@@ -86,19 +86,29 @@ __device__ __forceinline__ int v_offset(int dd, int u)
     return dd * (kBc * 2) + ((u ^ s) << 3);
 }
 
+// v_permlane32_swap_b32 a, b exchanges lanes 32..63 of a with lanes 0..31 of
+// b.  Starting from a = b = x this leaves a = [x_lo, x_lo], b = [x_hi, x_hi],
+// so op(a, b) combines lane l with lane l^32 in every lane.  Inline asm keeps
+// the two results apart: the compiler builtin called with one value for both
+// operands gets folded as if its two results were equal.
+__device__ __forceinline__ void half_swap(float &a, float &b)
+{
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+
 __device__ __forceinline__ float wave_half_max(float x)
 {
     // Lanes l and l^32 hold the two halves of one query's keys.
-    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
-                                                    __builtin_bit_cast(uint32_t, x), false, false);
-    return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+    float a = x, b = x;
+    half_swap(a, b);
+    return fmaxf(a, b);
 }
 
 __device__ __forceinline__ float wave_half_sum(float x)
 {
-    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
-                                                    __builtin_bit_cast(uint32_t, x), false, false);
-    return __builtin_bit_cast(float, r[0]) + __builtin_bit_cast(float, r[1]);
+    float a = x, b = x;
+    half_swap(a, b);
+    return a + b;
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
