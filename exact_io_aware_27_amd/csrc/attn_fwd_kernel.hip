@@ -3,7 +3,7 @@
 // One workgroup owns one (batch*head, query tile) pair and walks the key/value
 // tiles of that head in order (the FlashAttention-2 loop order and sequence
 // parallelism: "FlashAttention 1-4 evolution cheat sheet", argus-lessons,
-// FlashAttention-2 section).  Per key/value tile it forms the score tile on
+// FlashAttention-2 section).  Per key/value block it forms the score tile on
 // the matrix cores, keeps a running row max m and running sum l, rescales the
 // output accumulator by exp(m_old - m_new) and adds P V (the online softmax
 // iteration of the "FlashAttention" concept page, compassingai.com, section 3,
@@ -22,24 +22,27 @@
 //   * The probabilities leave the accumulator in the register order the PV
 //     MFMA wants for its B operand (O^T = V^T P^T), with no shuffle.
 //   * K and V tiles of 64 keys go straight from global memory to LDS
-//     (global_load_lds_dwordx4: no registers, no VALU), row-major with an XOR
-//     swizzle of 16-byte chunks.  K feeds the QK^T MFMA with ds_read_b128;
-//     V^T feeds the PV MFMA with ds_read_b64_tr_b16, the gfx950 transposing
-//     LDS read (within 16 lanes it hands lane j the element j%4 of source
-//     lanes j/4 + 4e), so V is never transposed in registers.
-//   * Software pipeline inside each wave: while the VALU computes the softmax
-//     of tile t, the matrix cores run Q K^T of tile t+1 and P V of tile t-1
-//     (the GEMM/softmax overlap of "FlashAttention 1-4 evolution cheat
-//     sheet", FlashAttention-3 section, done within one wave).  K is
-//     prefetched two tiles ahead and V one tile ahead, double-buffered.
+//     (global_load_lds_dwordx4: no registers, no VALU; a wave-uniform base in
+//     SGPRs plus a fixed per-lane offset), row-major with an XOR swizzle of
+//     16-byte chunks.  K feeds the QK^T MFMA with ds_read_b128; V^T feeds the
+//     PV MFMA with ds_read_b64_tr_b16, the gfx950 transposing LDS read
+//     (within 16 lanes it hands lane j the element j%4 of source lanes
+//     j/4 + 4e), so V is never transposed in registers.
+//   * Software pipeline inside each wave, in 32-key steps: while the VALU
+//     computes the softmax of block k, the matrix cores run Q K^T of block
+//     k+1 and P V of block k-1 (the GEMM/softmax overlap of "FlashAttention
+//     1-4 evolution cheat sheet", FlashAttention-3 section, done within one
+//     wave), with an explicit interleave of MFMAs, VALU work and operand
+//     reads.  K is prefetched two 64-key tiles ahead and V one tile ahead,
+//     double-buffered, one barrier per tile.
 //   * exp is v_exp_f32 (base 2) with scale*log2(e) folded into one FMA.
 //     The row max is exact at every 32-key block, so the largest probability
 //     of a row is exactly 1 and rounds to bf16 without error; the O rescale
 //     is skipped (a wave-uniform branch) when no row of the wave found a new
-//     max, the common case once a few hundred keys have been seen.  (A
-//     reference max that lags by up to 2^8, as in the conditional rescaling
-//     of the FlashAttention-4 section, leaves the dominant probability
-//     inexact in bf16 and breaks the 1e-2 bound on large-logit inputs.)
+//     max.  (A reference max that lags by up to 2^8, as in the conditional
+//     rescaling of the FlashAttention-4 section, leaves the dominant
+//     probability inexact in bf16 and breaks the 1e-2 bound on large-logit
+//     inputs.)
 //   * Causal: tiles entirely above the diagonal are never loaded; the mask
 //     is applied only in tiles that cross the diagonal or the sequence end.
 //   * Workgroup order: heaviest causal query tiles first (longest-processing-
@@ -71,50 +74,65 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWave * kWaves;
 constexpr int kRowsPerWave = 32;
 constexpr int kBr = kRowsPerWave * kWaves;  // query rows per workgroup
-constexpr int kBc = 64;                     // keys per K/V tile
+constexpr int kBc = 64;                     // keys per K/V tile (two 32-key blocks)
 constexpr int kXcds = 8;                    // MI355X: 8 XCDs, workgroups dealt round-robin
 constexpr float kNegInf = -__builtin_inff();
 
 template <int D>
 struct Tile {
     static constexpr int kRowBytes = D * 2;
-    static constexpr int kChunks = D / 8;              // 16-byte chunks per row
-    static constexpr int kBytes = kBc * kRowBytes;     // one K or V tile
-    static constexpr int kQkSteps = D / 16;            // MFMA k-steps of Q K^T
-    static constexpr int kOBlocks = D / 32;            // 32-row blocks of O^T
-    static constexpr int kRowsPerLoad = 1024 / kRowBytes;  // rows one wave-wide 16B load fills
+    static constexpr int kChunks = D / 8;                  // 16-byte chunks per row
+    static constexpr int kBytes = kBc * kRowBytes;         // one K or V tile
+    static constexpr int kQkSteps = D / 16;                // MFMA k-steps of Q K^T
+    static constexpr int kOBlocks = D / 32;                // 32-row blocks of O^T
+    static constexpr int kRowsPerLoad = 1024 / kRowBytes;  // rows one wave-wide 16-byte load fills
     static constexpr int kLoadsPerWave = kBytes / 1024 / kWaves;
 };
 
-// Chunk c of row r sits at chunk position c ^ swz(r).
-//  D = 128 (16 chunks): any 16 consecutive rows read at one chunk hit 16
-//    distinct positions (ds_read_b128), and 4 aligned rows read as chunk
-//    pairs {2u, 2u+1} hit 8 distinct positions (ds_read_b64_tr_b16).
-//  D = 64 (8 chunks): any 8 aligned rows are distinct and 4 aligned rows
-//    give distinct chunk pairs.
+// LDS tiles are row-major (one key per row, D*2 bytes) with 16-byte chunk c
+// of row r stored at chunk position c ^ swz(r).
+//  K tiles (read by ds_read_b128, lanes 0..15 on 16 consecutive rows at one
+//  chunk): D = 128 uses a 4-bit swizzle, distinct over any 16 consecutive
+//  rows; D = 64 (8 chunks, two rows per 256 bytes) uses one distinct over
+//  any aligned 8 rows and over (row parity, position) for 16 rows.
+//  V tiles (read by ds_read_b64_tr_b16, 16 lanes on 4 aligned rows x 2
+//  adjacent chunks {2u, 2u+1}): a 3-bit swizzle whose pairs are distinct
+//  over any 4 aligned rows; it leaves chunk bit 3 alone, so head-dim blocks
+//  64 apart are a fixed 128 bytes apart.
 template <int D>
-__device__ __forceinline__ int swz(int r)
+__device__ __forceinline__ int swz_k(int r)
 {
     if constexpr (D == 128)
         return ((r & 7) << 1) | ((r >> 3) & 1);
     else
-        return ((r & 3) << 1) | ((r >> 2) & 1);
+        return (r & 7) ^ ((r >> 3) & 1);
+}
+
+__device__ __forceinline__ int swz_v(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+template <int D>
+__device__ __forceinline__ int k_offset(int r, int c)
+{
+    return r * Tile<D>::kRowBytes + ((c ^ swz_k<D>(r)) << 4);
 }
 
 template <int D>
-__device__ __forceinline__ int tile_offset(int r, int c)
+__device__ __forceinline__ int v_offset(int r, int c)
 {
-    return r * Tile<D>::kRowBytes + ((c ^ swz<D>(r)) << 4);
+    return r * Tile<D>::kRowBytes + ((c ^ swz_v(r)) << 4);
 }
 
 // v_permlane32_swap_b32 a, b exchanges lanes 32..63 of a with lanes 0..31 of
 // b.  Starting from a = b = x this leaves a = [x_lo, x_lo], b = [x_hi, x_hi],
-// so op(a, b) combines lane l with lane l^32 in every lane.  Inline asm keeps
-// the two results apart: the compiler builtin called with one value for both
-// operands gets folded as if its two results were equal.
+// so op(a, b) combines lane l with lane l^32 in every lane.  It is issued as
+// inline asm with two read-write operands: the compiler builtin's second
+// result gets dropped when both operands carry the same value.  The asm is
+// not volatile, so the scheduler may move it like any VALU instruction; the
+// s_nops cover the VALU-write to permlane-read hazard the compiler cannot see
+// inside the asm.
 __device__ __forceinline__ void half_swap(float &a, float &b)
 {
-    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+    asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
 }
 
 __device__ __forceinline__ float wave_half_max(float x)
@@ -156,79 +174,19 @@ __device__ __forceinline__ void tile_of(int wg, int n_wg, int nqt, int &bh, int 
 // Issued through inline asm so the compiler does not treat it as a store that
 // may alias every later LDS read (it would wait for it before each one); the
 // kernel waits for these copies itself (s_waitcnt vmcnt before a barrier).
+// Two forms: a per-lane 64-bit address, or a wave-uniform base in SGPRs plus
+// a per-lane 32-bit offset (no per-lane address arithmetic in the loop).
 __device__ __forceinline__ void lds_dma16(const void *g, uint32_t lds_addr)
 {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr)
                  : "memory", "m0");
 }
 
-// One K or V tile (64 rows starting at key kv0) from global memory straight
-// into LDS.  Wave w issues kLoadsPerWave wave-wide 16-byte loads; lane L of a
-// load fills the L-th 16 bytes of its 1 KB slice, so the lane fetches the
-// global chunk that the swizzle places there.  Rows past N are clamped to
-// N-1: they are finite data whose probabilities are exactly 0.
-template <int D>
-__device__ __forceinline__ void load_tile(const __bf16 *src, int kv0, int N, uint32_t lds, int wave_u, int lane)
+__device__ __forceinline__ void lds_dma16(const void *sbase, uint32_t voff, uint32_t lds_addr)
 {
-    using T = Tile<D>;
-#pragma unroll
-    for (int i = 0; i < T::kLoadsPerWave; ++i) {
-        const int slice = wave_u * T::kLoadsPerWave + i;  // wave-uniform
-        const int r = slice * T::kRowsPerLoad + lane / T::kChunks;
-        const int pos = lane % T::kChunks;
-        const int c = pos ^ swz<D>(r);
-        const int key = min(kv0 + r, N - 1);
-        lds_dma16(src + (size_t)key * D + c * 8, lds + slice * 1024);
-    }
-}
-
-// S^T (32 keys x 32 queries) for the 32-key block at row rb of a K tile.
-template <int D>
-__device__ __forceinline__ f32x16 qk_block(const char *ks, int rb, const bf16x8 *qop, int n, int half)
-{
-    using T = Tile<D>;
-    f32x16 s = {};
-    const int r = rb + n;
-#pragma unroll
-    for (int st = 0; st < T::kQkSteps; ++st) {
-        const bf16x8 a = *LDS_PTR(const bf16x8, ks + tile_offset<D>(r, 2 * st + half));
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[st], s, 0, 0, 0);
-    }
-    return s;
-}
-
-// O^T += V^T P^T for the 32-key block at row rb of a V tile.  pb[ks] holds
-// the bf16 probabilities of keys rb + 16 ks + {8 jj + 4 half + e} in operand
-// position 8 half + 4 jj + e; the transposing reads hand the A operand the
-// same key order (source lane i of a 16-lane group reads row i/4 of its 4-key
-// group, head-dim columns 4 (i%4) .. +3).
-template <int D>
-__device__ __forceinline__ void pv_block(const char *vs, int rb, const bf16x8 *pb, f32x16 *oacc, int lane)
-{
-    using T = Tile<D>;
-    const int g = lane >> 4;  // 16-lane group
-    const int i = lane & 15;  // source lane within the group
-    const int h = g >> 1;     // key half of the operand (lanes 32..63)
-    const int dh = g & 1;     // which 16 of the block's 32 head-dim rows
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-        for (int b = 0; b < T::kOBlocks; ++b) {
-            s16x4 part[2];
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                const int r = rb + 16 * ks + 8 * jj + 4 * h + (i >> 2);
-                const int dcol = 32 * b + 16 * dh + 4 * (i & 3);
-                const int off = tile_offset<D>(r, dcol >> 3) + ((dcol & 4) << 1);
-                part[jj] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vs + off));
-            }
-            const u32x2 lo = __builtin_bit_cast(u32x2, part[0]);
-            const u32x2 hi = __builtin_bit_cast(u32x2, part[1]);
-            const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
-            oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va), pb[ks], oacc[b],
-                                                              0, 0, 0);
-        }
-    }
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+                 "s"(lds_addr)
+                 : "memory", "m0");
 }
 
 template <int D, bool CAUSAL>
@@ -237,13 +195,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     __bf16 *__restrict__ O, float *__restrict__ LSE, int N, int n_wg, int nqt, float c_log2)
 {
     using T = Tile<D>;
-    // K buffers 0, 1 then V buffers 0, 1.
+    // LDS: K buffers 0, 1 then V buffers 0, 1, each one 64-key tile.
     __shared__ __attribute__((aligned(1024))) char smem[4 * T::kBytes];
+    constexpr int kKBuf0 = 0, kVBuf0 = 2 * T::kBytes;
     const uint32_t smem_lds = (uint32_t)(uintptr_t)LDS_PTR(char, smem);
-    auto kbuf = [&](int i) { return smem + i * T::kBytes; };
-    auto vbuf = [&](int i) { return smem + (2 + i) * T::kBytes; };
-    auto kbuf_lds = [&](int i) { return smem_lds + i * T::kBytes; };
-    auto vbuf_lds = [&](int i) { return smem_lds + (2 + i) * T::kBytes; };
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -256,8 +211,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     tile_of(blockIdx.x, n_wg, nqt, bh, qt);
     const int q0 = qt * kBr;
     const size_t head = (size_t)bh * (size_t)N * D;
-    const __bf16 *Kh = K + head;
-    const __bf16 *Vh = V + head;
+    const char *Kh = reinterpret_cast<const char *>(K + head);
+    const char *Vh = reinterpret_cast<const char *>(V + head);
 
     const int qw0 = q0 + wave * kRowsPerWave;  // first query of this wave
     const int qidx = qw0 + n;
@@ -265,13 +220,73 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
 
     const int kv_end = CAUSAL ? min(N, q0 + kBr) : N;
     const int ntiles = (kv_end + kBc - 1) / kBc;
-    const int nblocks = 2 * ntiles;  // 32-key pipeline steps
 
-    // Prologue: K tiles 0 and 1 and V tile 0 in flight while Q is read.
-    load_tile<D>(Kh, 0, N, kbuf_lds(0), wave_u, lane);
+    // ---- per-lane offsets, fixed for the whole loop ----
+    // DMA: slice i of this wave is LDS bytes [1024 s, 1024 s + 1024) of a tile
+    // (s = wave * kLoadsPerWave + i); the lane fetches row r, chunk c.
+    uint32_t kdma[T::kLoadsPerWave], vdma[T::kLoadsPerWave];
+#pragma unroll
+    for (int i = 0; i < T::kLoadsPerWave; ++i) {
+        const int slice = wave * T::kLoadsPerWave + i;
+        const int r = slice * T::kRowsPerLoad + lane / T::kChunks;
+        const int pos = lane % T::kChunks;
+        kdma[i] = r * T::kRowBytes + ((pos ^ swz_k<D>(r)) << 4);
+        vdma[i] = r * T::kRowBytes + ((pos ^ swz_v(r)) << 4);
+    }
+    // K operand of S^T = K Q^T: row n of a 32-key block, chunk 2 st + half.
+    uint32_t koff[T::kQkSteps];
+#pragma unroll
+    for (int st = 0; st < T::kQkSteps; ++st)
+        koff[st] = k_offset<D>(n, 2 * st + half);
+    // V^T operand through ds_read_b64_tr_b16: source lane i of 16-lane group
+    // g reads key row 8 jj + 4 (g / 2) + i / 4 of a 16-key step, head-dim
+    // columns 32 b + 16 (g % 2) + 4 (i % 4) .. +3.  Blocks b and b+2 are 128
+    // bytes apart (the V swizzle keeps chunk bit 3).
+    uint32_t voff[2][2];
+    {
+        const int g = lane >> 4, i = lane & 15;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const int r = 8 * jj + 4 * (g >> 1) + (i >> 2);
+                const int dcol = 32 * b + 16 * (g & 1) + 4 * (i & 3);
+                voff[b][jj] = v_offset<D>(r, dcol >> 3) + ((dcol & 4) << 1);
+            }
+    }
+    auto vread = [&](int byte, int b, int jj) {  // 4 keys x 1 head-dim column, transposed
+        return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            LDS_PTR(s16x4, smem + byte + 128 * (b >> 1) + voff[b & 1][jj]));
+    };
+
+    // One K or V tile (64 keys from kv0) into the LDS buffer at byte lds_buf.
+    // Rows past N (only in the last tile) are clamped to N-1: finite data
+    // whose probabilities are exactly 0.
+    auto load_tile = [&](const char *src, int kv0, int lds_buf, const uint32_t *dma) {
+        const uint32_t lds = smem_lds + lds_buf + wave_u * T::kLoadsPerWave * 1024;
+        if (kv0 + kBc <= N) {
+            const char *base = src + (size_t)kv0 * T::kRowBytes;
+#pragma unroll
+            for (int i = 0; i < T::kLoadsPerWave; ++i)
+                lds_dma16(base, dma[i], lds + i * 1024);
+        } else {
+#pragma unroll
+            for (int i = 0; i < T::kLoadsPerWave; ++i) {
+                const int key = min(kv0 + (int)(dma[i] / T::kRowBytes), N - 1);
+                lds_dma16(src + (size_t)key * T::kRowBytes + (dma[i] % T::kRowBytes), lds + i * 1024);
+            }
+        }
+    };
+
+    // Prologue: K tiles 0 and 1 and V tile 0 in flight while Q is read; V
+    // buffer 1 is zeroed for the first step's (empty) P V.
+    load_tile(Kh, 0, kKBuf0, kdma);
     if (ntiles > 1)
-        load_tile<D>(Kh, kBc, N, kbuf_lds(1), wave_u, lane);
-    load_tile<D>(Vh, 0, N, vbuf_lds(0), wave_u, lane);
+        load_tile(Kh, kBc, kKBuf0 + T::kBytes, kdma);
+    load_tile(Vh, 0, kVBuf0, vdma);
+#pragma unroll
+    for (int i = 0; i < T::kBytes / (16 * kThreads); ++i)
+        *LDS_PTR(u32x4, smem + kVBuf0 + T::kBytes + 16 * (tid + i * kThreads)) = u32x4{};
 
     // Q^T operand, resident for the whole key loop: k-step s holds
     // q[qidx][16 s + 8 half .. +7] (zeros past N).
@@ -288,33 +303,52 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    f32x16 sc = qk_block<D>(kbuf(0), 0, qop, n, half);  // scores of block 0
+    f32x16 sc = {};  // scores of the block being turned into probabilities
+#pragma unroll
+    for (int st = 0; st < T::kQkSteps; ++st)
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*LDS_PTR(const bf16x8, smem + kKBuf0 + koff[st]), qop[st], sc,
+                                                     0, 0, 0);
     f32x16 oacc[T::kOBlocks];
 #pragma unroll
     for (int b = 0; b < T::kOBlocks; ++b)
         oacc[b] = f32x16{};
-    float m_ref = kNegInf;  // reference max, log2 units (scores times c_log2)
+    float m_ref = kNegInf;  // running max, log2 units (scores times c_log2)
     float l_run = 0.f;      // running sum over this lane's half of the keys
     bf16x8 pb_prev[2] = {bf16x8{}, bf16x8{}};  // P of the previous block (none yet: zeros)
 
-    // One 32-key pipeline step, straight-line code so that the softmax of
-    // block k (VALU) interleaves with the scores of block k+1 and P V of block
-    // k-1 (matrix cores).  At the ends the block indices are clamped: the
-    // first step multiplies V block 0 by P = 0, the last recomputes scores it
-    // discards.  MASKED steps apply the causal / sequence-end mask and also
-    // serve non-positive scales.
-    auto step = [&](int k, auto masked_tag) {
-        constexpr bool MASKED = decltype(masked_tag)::value;
-        const int kq = min(k + 1, nblocks - 1);
-        const int kp = max(k - 1, 0);
-        const char *kq_buf = kbuf((kq >> 1) & 1);
-        const int kq_row = 32 * (kq & 1);
+    // O^T += V^T P^T over the 32 keys of one block (two 16-key k-steps);
+    // vp is the LDS byte of the block's first V row.
+    auto pv = [&](int vp, const bf16x8 *pbk) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+            for (int b = 0; b < T::kOBlocks; ++b) {
+                const int vb = vp + ks * 16 * T::kRowBytes;
+                const u32x2 lo = __builtin_bit_cast(u32x2, vread(vb, b, 0));
+                const u32x2 hi = __builtin_bit_cast(u32x2, vread(vb, b, 1));
+                const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
+                oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va), pbk[ks], oacc[b],
+                                                                  0, 0, 0);
+            }
+        }
+    };
 
-        // K operands of block k+1, read early so their latency hides under the softmax.
-        bf16x8 kop[T::kQkSteps];
+    // One 32-key pipeline step (block k): the softmax of block k on the VALU
+    // interleaves with the matrix-core work of the scores of block k+1 (K at
+    // LDS byte kq) and P V of block k-1 (V at LDS byte vp).  The first step
+    // multiplies the zeroed V buffer by P = 0; the last computes scores of a
+    // block that does not exist and discards them.  MASKED steps apply the
+    // causal / sequence-end mask and also serve non-positive scales.
+    auto step = [&](int k, int kq, int vp, auto masked_tag) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
+        // Keep the per-lane LDS offsets opaque inside the loop: otherwise
+        // their sums with each buffer's constant base are hoisted out of the
+        // loop as separate registers instead of riding in the ds_read
+        // immediate offset field.
 #pragma unroll
         for (int st = 0; st < T::kQkSteps; ++st)
-            kop[st] = *LDS_PTR(const bf16x8, kq_buf + tile_offset<D>(kq_row + n, 2 * st + half));
+            asm volatile("" : "+v"(koff[st]));
+        asm volatile("" : "+v"(voff[0][0]), "+v"(voff[0][1]), "+v"(voff[1][0]), "+v"(voff[1][1]));
 
         // Register 4j+e holds key 32 k + 8 j + 4 half + e.
         float mx;
@@ -365,12 +399,27 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
         f32x16 sn = {};
 #pragma unroll
         for (int st = 0; st < T::kQkSteps; ++st)
-            sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[st], qop[st], sn, 0, 0, 0);
-        pv_block<D>(vbuf((kp >> 1) & 1), 32 * (kp & 1), pb_prev, oacc, lane);
+            sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*LDS_PTR(const bf16x8, smem + kq + koff[st]), qop[st],
+                                                         sn, 0, 0, 0);
+        pv(vp, pb_prev);
         sc = sn;
-
         l_run = alpha * l_run + rowsum;
-        if (rescale) {  // after P V of block k-1, which was relative to the old reference
+
+        // Issue order for this step's scheduling region: the 16 MFMAs (8 for
+        // the next scores, 8 for P V) each followed by a share of the softmax
+        // VALU work, so the matrix cores and the VALU stay busy together; the
+        // operand reads (8 ds_read_b128 of K, 16 ds_read_b64_tr_b16 of V) run
+        // about two MFMAs ahead of their use, hiding LDS latency with a
+        // bounded number of registers in flight.
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS read
+#pragma unroll
+        for (int i = 0; i < 2 * T::kQkSteps; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);  // VALU incl. transcendental
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+        }
+
+        if (rescale) {  // after P V of block k-1, which was relative to the old max
 #pragma unroll
             for (int b = 0; b < T::kOBlocks; ++b)
                 oacc[b] *= alpha;
@@ -379,33 +428,45 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
         pb_prev[1] = pb[1];
     };
 
-    // One 64-key tile = two steps.  The even step makes the last reads of K
-    // tile t and V tile t-1; after the barrier those buffers are refilled
-    // with K tile t+2 and V tile t+1, which land before the next barrier.
-    auto tile = [&](int t, auto masked_tag) {
-        step(2 * t, masked_tag);
+    // One 64-key tile t held in K buffer P = t % 2 (V tile t-1 in V buffer
+    // 1-P).  The even step makes the last reads of K tile t and V tile t-1;
+    // after the barrier those buffers are refilled with K tile t+2 and V tile
+    // t+1, which land before the next barrier.
+    auto tile = [&](int t, auto parity_tag, auto masked_tag) {
+        constexpr int P = decltype(parity_tag)::value;
+        constexpr int kHalf = 32 * T::kRowBytes;
+        step(2 * t, kKBuf0 + P * T::kBytes + kHalf, kVBuf0 + (1 - P) * T::kBytes + kHalf, masked_tag);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (t + 2 < ntiles)
-            load_tile<D>(Kh, (t + 2) * kBc, N, kbuf_lds(t & 1), wave_u, lane);
+            load_tile(Kh, (t + 2) * kBc, kKBuf0 + P * T::kBytes, kdma);
         if (t + 1 < ntiles)
-            load_tile<D>(Vh, (t + 1) * kBc, N, vbuf_lds((t + 1) & 1), wave_u, lane);
-        step(2 * t + 1, masked_tag);
+            load_tile(Vh, (t + 1) * kBc, kVBuf0 + (1 - P) * T::kBytes, vdma);
+        step(2 * t + 1, kKBuf0 + (1 - P) * T::kBytes, kVBuf0 + P * T::kBytes, masked_tag);
     };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
 
     // Tiles [0, t_free) need no mask: below the causal diagonal of every
-    // query of the workgroup and wholly inside the sequence.
+    // query of the workgroup and wholly inside the sequence.  t_free is made
+    // even so that both loops walk (buffer 0, buffer 1) tile pairs.
     int t_free = N / kBc;
     if (CAUSAL)
         t_free = min(t_free, (q0 + 1) / kBc);
     if (!(c_log2 > 0.f))
         t_free = 0;
-    t_free = min(t_free, ntiles);
-    for (int t = 0; t < t_free; ++t)
-        tile(t, std::false_type{});
-    for (int t = t_free; t < ntiles; ++t)
-        tile(t, std::true_type{});
-    pv_block<D>(vbuf((ntiles - 1) & 1), 32, pb_prev, oacc, lane);
+    t_free = min(t_free, ntiles) & ~1;
+    for (int t = 0; t < t_free; t += 2) {
+        tile(t, P0{}, std::false_type{});
+        tile(t + 1, P1{}, std::false_type{});
+    }
+    for (int t = t_free; t < ntiles; t += 2) {
+        tile(t, P0{}, std::true_type{});
+        if (t + 1 < ntiles)
+            tile(t + 1, P1{}, std::true_type{});
+    }
+    // P V of the last block: second half of V tile ntiles-1.
+    pv(kVBuf0 + ((ntiles - 1) & 1) * T::kBytes + 32 * T::kRowBytes, pb_prev);
 
     // Epilogue: O = O / l, LSE = ln2 * (m + log2 l).
     const float l_tot = wave_half_sum(l_run);
