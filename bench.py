@@ -52,6 +52,46 @@ def measured_traffic():
     return t.get("hbm_bytes_per_launch")
 
 
+def pmc_summary(fetch_csv, write_csv, copy_mib, out_json=TRAFFIC_FILE):
+    """HBM bytes per attn_fwd launch from two rocprofv3 --pmc runs (FETCH_SIZE,
+    then WRITE_SIZE, both in KiB per dispatch), each scaled by what the same
+    counter reads for the plain device copy of copy_mib MiB that bench.py runs
+    with --copy-calibration-mib (an elementwise kernel that reads and writes
+    copy_mib MiB; the largest non-attention dispatch of each run).  Writes
+    out_json and returns the summary."""
+    import csv
+
+    def per_dispatch(path, counter):
+        attn, copy = [], []
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                name = r["Kernel_Name"]
+                if "attn_fwd_kernel" in name:
+                    attn.append(float(r["Counter_Value"]))
+                else:  # the fill and the copy of the calibration buffer
+                    copy.append(float(r["Counter_Value"]))
+        if not attn or not copy:
+            raise SystemExit("%s: no %s rows for attn_fwd_kernel and the calibration copy" % (path, counter))
+        return sum(attn) / len(attn), max(copy)
+
+    known = copy_mib * 1024.0  # KiB moved each way by the copy
+    fa, fc = per_dispatch(fetch_csv, "FETCH_SIZE")
+    wa, wc = per_dispatch(write_csv, "WRITE_SIZE")
+    f_fetch, f_write = known / fc, known / wc
+    total = (fa * f_fetch + wa * f_write) * 1024.0
+    summary = {"kernel_hash": kernel_hash(), "workload": "long_causal B=2 H=32 N=8192 d=128 causal",
+               "fetch_kib_per_launch": fa, "write_kib_per_launch": wa,
+               "copy_mib": copy_mib, "copy_fetch_kib": fc, "copy_write_kib": wc,
+               "fetch_scale": f_fetch, "write_scale": f_write,
+               "hbm_bytes_per_launch": total}
+    with open(out_json, "w") as f:
+        json.dump(summary, f, indent=1)
+        f.write("\n")
+    return summary
+
+
 def cpu_baseline(w, q, k, v, o_gpu, lse_gpu, rows_per_head):
     """Time the fp64 oracle on a bounded, seeded row sample of the same workload;
     the same rows double as a parity check of the timed launch's output."""
@@ -96,7 +136,15 @@ def main():
                     help="query rows per head in the oracle's CPU-baseline sample (0: skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (HBM counter calibration)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: turn two rocprofv3 counter CSVs (FETCH_SIZE run, WRITE_SIZE run, "
+                         "both with --copy-calibration-mib) into HBM bytes per launch")
     args = ap.parse_args()
+
+    if args.pmc_summary:
+        print(json.dumps(pmc_summary(args.pmc_summary[0], args.pmc_summary[1],
+                                     args.copy_calibration_mib or 1024)))
+        return 0
 
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
@@ -125,7 +173,7 @@ def main():
         n = args.copy_calibration_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
-        dst.copy_(src)
+        torch.bitwise_not(src, out=dst)  # an elementwise kernel: reads n bytes, writes n bytes
         torch.cuda.synchronize()
         del src, dst
 
