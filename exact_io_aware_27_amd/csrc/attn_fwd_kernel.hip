@@ -22,12 +22,16 @@
 //   * The probabilities leave the accumulator in the register order the PV
 //     MFMA wants for its B operand (O^T = V^T P^T), with no shuffle.
 //   * K and V tiles of 64 keys go straight from global memory to LDS
-//     (global_load_lds_dwordx4: no registers, no VALU; a wave-uniform base in
-//     SGPRs plus a fixed per-lane offset), row-major with an XOR swizzle of
-//     16-byte chunks.  K feeds the QK^T MFMA with ds_read_b128; V^T feeds the
-//     PV MFMA with ds_read_b64_tr_b16, the gfx950 transposing LDS read
-//     (within 16 lanes it hands lane j the element j%4 of source lanes
-//     j/4 + 4e), so V is never transposed in registers.
+//     (buffer_load_dwordx4 ... lds: no registers, no VALU; a fixed per-lane
+//     offset plus a per-tile SGPR offset, range-checked against the head so
+//     rows past N read as zeros), row-major with an XOR swizzle of 16-byte
+//     chunks.  The four LDS buffers are separate arrays, so the compiler can
+//     see that a copy into one buffer never aliases reads of another and
+//     schedules the copies among the MFMAs of a step without waiting on
+//     them.  K feeds the QK^T MFMA with ds_read_b128; V^T feeds the PV MFMA
+//     with ds_read_b64_tr_b16, the gfx950 transposing LDS read (within 16
+//     lanes it hands lane j the element j%4 of source lanes j/4 + 4e), so V
+//     is never transposed in registers.
 //   * Software pipeline inside each wave, in 32-key steps: while the VALU
 //     computes the softmax of block k, the matrix cores run Q K^T of block
 //     k+1 and P V of block k-1 (the GEMM/softmax overlap of "FlashAttention
@@ -77,6 +81,9 @@ constexpr int kBr = kRowsPerWave * kWaves;  // query rows per workgroup
 constexpr int kBc = 64;                     // keys per K/V tile (two 32-key blocks)
 constexpr int kXcds = 8;                    // MI355X: 8 XCDs, workgroups dealt round-robin
 constexpr float kNegInf = -__builtin_inff();
+// Buffer-resource word 3 for raw (unformatted, stride-0) 32-bit loads with
+// out-of-range offsets returning zero.
+constexpr int kBufferFlags = 0x00020000;
 
 template <int D>
 struct Tile {
@@ -169,36 +176,21 @@ __device__ __forceinline__ void tile_of(int wg, int n_wg, int nqt, int &bh, int 
     qt = nqt - 1 - lin % nqt;
 }
 
-// Global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane L
-// writes bytes [16 L, 16 L + 16) after the wave-uniform LDS address in M0.
-// Issued through inline asm so the compiler does not treat it as a store that
-// may alias every later LDS read (it would wait for it before each one); the
-// kernel waits for these copies itself (s_waitcnt vmcnt before a barrier).
-// Two forms: a per-lane 64-bit address, or a wave-uniform base in SGPRs plus
-// a per-lane 32-bit offset (no per-lane address arithmetic in the loop).
-__device__ __forceinline__ void lds_dma16(const void *g, uint32_t lds_addr)
-{
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr)
-                 : "memory", "m0");
-}
-
-__device__ __forceinline__ void lds_dma16(const void *sbase, uint32_t voff, uint32_t lds_addr)
-{
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
-                 "s"(lds_addr)
-                 : "memory", "m0");
-}
-
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
     __bf16 *__restrict__ O, float *__restrict__ LSE, int N, int n_wg, int nqt, float c_log2)
 {
+    // The body is device code only (gfx950 buffer resources and LDS builtins);
+    // the host pass needs just the declaration to emit the launch stub.
+#if defined(__HIP_DEVICE_COMPILE__)
     using T = Tile<D>;
-    // LDS: K buffers 0, 1 then V buffers 0, 1, each one 64-key tile.
-    __shared__ __attribute__((aligned(1024))) char smem[4 * T::kBytes];
-    constexpr int kKBuf0 = 0, kVBuf0 = 2 * T::kBytes;
-    const uint32_t smem_lds = (uint32_t)(uintptr_t)LDS_PTR(char, smem);
+    // LDS: K buffers 0, 1 and V buffers 0, 1, each one 64-key tile, as four
+    // separate arrays (see the header comment).
+    __shared__ __attribute__((aligned(1024))) char sk0[T::kBytes];
+    __shared__ __attribute__((aligned(1024))) char sk1[T::kBytes];
+    __shared__ __attribute__((aligned(1024))) char sv0[T::kBytes];
+    __shared__ __attribute__((aligned(1024))) char sv1[T::kBytes];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -211,8 +203,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     tile_of(blockIdx.x, n_wg, nqt, bh, qt);
     const int q0 = qt * kBr;
     const size_t head = (size_t)bh * (size_t)N * D;
-    const char *Kh = reinterpret_cast<const char *>(K + head);
-    const char *Vh = reinterpret_cast<const char *>(V + head);
+    // Copies go through buffer resources over this head's K and V: offsets at
+    // or past N rows are out of range and read as zeros.
+    const int head_bytes = N * T::kRowBytes;
+    const __bf16 *Kh = K + head;
+    const __bf16 *Vh = V + head;
 
     const int qw0 = q0 + wave * kRowsPerWave;  // first query of this wave
     const int qidx = qw0 + n;
@@ -254,39 +249,33 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
                 voff[b][jj] = v_offset<D>(r, dcol >> 3) + ((dcol & 4) << 1);
             }
     }
-    auto vread = [&](int byte, int b, int jj) {  // 4 keys x 1 head-dim column, transposed
+    auto vread = [&](const char *buf, int byte, int b, int jj) __attribute__((always_inline)) {  // 4 keys x 1 head-dim column, transposed
         return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            LDS_PTR(s16x4, smem + byte + 128 * (b >> 1) + voff[b & 1][jj]));
+            LDS_PTR(s16x4, buf + byte + 128 * (b >> 1) + voff[b & 1][jj]));
     };
 
-    // One K or V tile (64 keys from kv0) into the LDS buffer at byte lds_buf.
-    // Rows past N (only in the last tile) are clamped to N-1: finite data
-    // whose probabilities are exactly 0.
-    auto load_tile = [&](const char *src, int kv0, int lds_buf, const uint32_t *dma) {
-        const uint32_t lds = smem_lds + lds_buf + wave_u * T::kLoadsPerWave * 1024;
-        if (kv0 + kBc <= N) {
-            const char *base = src + (size_t)kv0 * T::kRowBytes;
+    // One K or V tile (64 keys from kv0) into an LDS buffer: this wave's
+    // kLoadsPerWave 1 KB slices, each one buffer_load_dwordx4 ... lds.  Rows
+    // past N, and whole tiles past the end, read as zeros (no memory access),
+    // so the copy needs no branch.
+    auto load_tile = [&](const __bf16 *src, int kv0, char *buf, const uint32_t *dma) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t rsrc =
+            __builtin_amdgcn_make_buffer_rsrc((void *)src, (short)0, head_bytes, kBufferFlags);
 #pragma unroll
-            for (int i = 0; i < T::kLoadsPerWave; ++i)
-                lds_dma16(base, dma[i], lds + i * 1024);
-        } else {
-#pragma unroll
-            for (int i = 0; i < T::kLoadsPerWave; ++i) {
-                const int key = min(kv0 + (int)(dma[i] / T::kRowBytes), N - 1);
-                lds_dma16(src + (size_t)key * T::kRowBytes + (dma[i] % T::kRowBytes), lds + i * 1024);
-            }
-        }
+        for (int i = 0; i < T::kLoadsPerWave; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc, LDS_PTR(void, buf + (wave_u * T::kLoadsPerWave + i) * 1024), 16, dma[i],
+                kv0 * T::kRowBytes, 0, 0);
     };
 
     // Prologue: K tiles 0 and 1 and V tile 0 in flight while Q is read; V
     // buffer 1 is zeroed for the first step's (empty) P V.
-    load_tile(Kh, 0, kKBuf0, kdma);
-    if (ntiles > 1)
-        load_tile(Kh, kBc, kKBuf0 + T::kBytes, kdma);
-    load_tile(Vh, 0, kVBuf0, vdma);
+    load_tile(Kh, 0, sk0, kdma);
+    load_tile(Kh, kBc, sk1, kdma);
+    load_tile(Vh, 0, sv0, vdma);
 #pragma unroll
     for (int i = 0; i < T::kBytes / (16 * kThreads); ++i)
-        *LDS_PTR(u32x4, smem + kVBuf0 + T::kBytes + 16 * (tid + i * kThreads)) = u32x4{};
+        *LDS_PTR(u32x4, sv1 + 16 * (tid + i * kThreads)) = u32x4{};
 
     // Q^T operand, resident for the whole key loop: k-step s holds
     // q[qidx][16 s + 8 half .. +7] (zeros past N).
@@ -306,8 +295,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     f32x16 sc = {};  // scores of the block being turned into probabilities
 #pragma unroll
     for (int st = 0; st < T::kQkSteps; ++st)
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*LDS_PTR(const bf16x8, smem + kKBuf0 + koff[st]), qop[st], sc,
-                                                     0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*LDS_PTR(const bf16x8, sk0 + koff[st]), qop[st], sc, 0, 0, 0);
     f32x16 oacc[T::kOBlocks];
 #pragma unroll
     for (int b = 0; b < T::kOBlocks; ++b)
@@ -317,15 +305,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     bf16x8 pb_prev[2] = {bf16x8{}, bf16x8{}};  // P of the previous block (none yet: zeros)
 
     // O^T += V^T P^T over the 32 keys of one block (two 16-key k-steps);
-    // vp is the LDS byte of the block's first V row.
-    auto pv = [&](int vp, const bf16x8 *pbk) {
+    // the block's first V row is at byte vp of V buffer vbuf.
+    auto pv = [&](const char *vbuf, int vp, const bf16x8 *pbk) __attribute__((always_inline)) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
             for (int b = 0; b < T::kOBlocks; ++b) {
                 const int vb = vp + ks * 16 * T::kRowBytes;
-                const u32x2 lo = __builtin_bit_cast(u32x2, vread(vb, b, 0));
-                const u32x2 hi = __builtin_bit_cast(u32x2, vread(vb, b, 1));
+                const u32x2 lo = __builtin_bit_cast(u32x2, vread(vbuf, vb, b, 0));
+                const u32x2 hi = __builtin_bit_cast(u32x2, vread(vbuf, vb, b, 1));
                 const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
                 oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va), pbk[ks], oacc[b],
                                                                   0, 0, 0);
@@ -334,13 +322,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     };
 
     // One 32-key pipeline step (block k): the softmax of block k on the VALU
-    // interleaves with the matrix-core work of the scores of block k+1 (K at
-    // LDS byte kq) and P V of block k-1 (V at LDS byte vp).  The first step
-    // multiplies the zeroed V buffer by P = 0; the last computes scores of a
-    // block that does not exist and discards them.  MASKED steps apply the
-    // causal / sequence-end mask and also serve non-positive scales.
-    auto step = [&](int k, int kq, int vp, auto masked_tag) {
+    // interleaves with the matrix-core work of the scores of block k+1 (K rows
+    // from byte kq of buffer kbuf) and P V of block k-1 (V rows from byte vp of
+    // buffer vbuf).  The first step multiplies the zeroed V buffer by P = 0;
+    // the last computes scores of a block that does not exist and discards
+    // them.  MASKED steps apply the causal / sequence-end mask and also serve
+    // non-positive scales.  LOADS steps also copy K tile load_t+1 into kdst
+    // and V tile load_t into vdst, spread among their MFMAs.
+    auto step = [&](int k, const char *kbuf, int kq, const char *vbuf, int vp, auto masked_tag, auto loads_tag,
+                    int load_t, char *kdst, char *vdst) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked_tag)::value;
+        constexpr bool LOADS = decltype(loads_tag)::value;
         // Keep the per-lane LDS offsets opaque inside the loop: otherwise
         // their sums with each buffer's constant base are hoisted out of the
         // loop as separate registers instead of riding in the ds_read
@@ -349,6 +341,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
         for (int st = 0; st < T::kQkSteps; ++st)
             asm volatile("" : "+v"(koff[st]));
         asm volatile("" : "+v"(voff[0][0]), "+v"(voff[0][1]), "+v"(voff[1][0]), "+v"(voff[1][1]));
+        // Pin the softmax inside its step: without this, loop rotation moves
+        // the first step's VALU work into the previous iteration's latch, away
+        // from the MFMAs it is meant to overlap.
+        asm volatile("" : "+v"(sc));
 
         // Register 4j+e holds key 32 k + 8 j + 4 half + e.
         float mx;
@@ -396,12 +392,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
             pb[ks] = __builtin_bit_cast(bf16x8, w);
         }
 
+        if constexpr (LOADS) {
+            load_tile(Kh, (load_t + 1) * kBc, kdst, kdma);
+            load_tile(Vh, load_t * kBc, vdst, vdma);
+        }
         f32x16 sn = {};
 #pragma unroll
         for (int st = 0; st < T::kQkSteps; ++st)
-            sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*LDS_PTR(const bf16x8, smem + kq + koff[st]), qop[st],
+            sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*LDS_PTR(const bf16x8, kbuf + kq + koff[st]), qop[st],
                                                          sn, 0, 0, 0);
-        pv(vp, pb_prev);
+        pv(vbuf, vp, pb_prev);
         sc = sn;
         l_run = alpha * l_run + rowsum;
 
@@ -417,6 +417,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
             __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);  // VALU incl. transcendental
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+            if (LOADS && i < 2 * T::kLoadsPerWave)
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // tile copy (VMEM)
         }
 
         if (rescale) {  // after P V of block k-1, which was relative to the old max
@@ -430,19 +432,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
 
     // One 64-key tile t held in K buffer P = t % 2 (V tile t-1 in V buffer
     // 1-P).  The even step makes the last reads of K tile t and V tile t-1;
-    // after the barrier those buffers are refilled with K tile t+2 and V tile
-    // t+1, which land before the next barrier.
-    auto tile = [&](int t, auto parity_tag, auto masked_tag) {
+    // after the barrier the odd step refills those buffers with K tile t+2 and
+    // V tile t+1 (past the end: zeros, no memory traffic), which land before
+    // the next barrier.
+    auto tile = [&](int t, auto parity_tag, auto masked_tag) __attribute__((always_inline)) {
         constexpr int P = decltype(parity_tag)::value;
         constexpr int kHalf = 32 * T::kRowBytes;
-        step(2 * t, kKBuf0 + P * T::kBytes + kHalf, kVBuf0 + (1 - P) * T::kBytes + kHalf, masked_tag);
+        char *kp = P ? sk1 : sk0, *kq = P ? sk0 : sk1;
+        char *vp = P ? sv1 : sv0, *vq = P ? sv0 : sv1;
+        step(2 * t, kp, kHalf, vq, kHalf, masked_tag, std::false_type{}, 0, kp, vq);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (t + 2 < ntiles)
-            load_tile(Kh, (t + 2) * kBc, kKBuf0 + P * T::kBytes, kdma);
-        if (t + 1 < ntiles)
-            load_tile(Vh, (t + 1) * kBc, kVBuf0 + (1 - P) * T::kBytes, vdma);
-        step(2 * t + 1, kKBuf0 + (1 - P) * T::kBytes, kVBuf0 + P * T::kBytes, masked_tag);
+        step(2 * t + 1, kq, 0, vp, 0, masked_tag, std::true_type{}, t + 1, kp, vq);
     };
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
@@ -466,7 +467,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
             tile(t + 1, P1{}, std::true_type{});
     }
     // P V of the last block: second half of V tile ntiles-1.
-    pv(kVBuf0 + ((ntiles - 1) & 1) * T::kBytes + 32 * T::kRowBytes, pb_prev);
+    pv((ntiles - 1) & 1 ? sv1 : sv0, 32 * T::kRowBytes, pb_prev);
+    __builtin_amdgcn_s_waitcnt(0);  // no copy may still be writing LDS when the workgroup ends
 
     // Epilogue: O = O / l, LSE = ln2 * (m + log2 l).
     const float l_tot = wave_half_sum(l_run);
@@ -486,6 +488,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     }
     if (LSE != nullptr && half == 0)
         LSE[(size_t)bh * N + qidx] = (m_ref + __builtin_log2f(l_tot)) * 0.69314718055994530942f;
+#endif
 }
 
 template <int D, bool CAUSAL>
