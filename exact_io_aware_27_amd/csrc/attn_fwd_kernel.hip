@@ -377,13 +377,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
         // Unmasked blocks hold raw scores (p = exp2(s c - m)); masked ones hold s c already.
         const float cmul = MASKED ? 1.f : c_log2;
 
-        float rowsum = 0.f;
         float p[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
+        for (int r = 0; r < 16; ++r)
             p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], cmul, -m_use));
-            rowsum += p[r];  // l sums fp32 p, before the bf16 rounding used by P V
+        // l sums fp32 p, before the bf16 rounding used by P V (two chains).
+        float rs0 = p[0], rs1 = p[1];
+#pragma unroll
+        for (int r = 2; r < 16; r += 2) {
+            rs0 += p[r];
+            rs1 += p[r + 1];
         }
+        const float rowsum = rs0 + rs1;
         bf16x8 pb[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -420,6 +425,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
             if (LOADS && i < 2 * T::kLoadsPerWave)
                 __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // tile copy (VMEM)
         }
+
+        // Keep this block's P and row sum inside this step: otherwise the
+        // compiler sinks the exps and adds next to their first uses (the next
+        // step's P V and the loop latch), where no MFMA is left to hide them.
+        asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(l_run));
 
         if (rescale) {  // after P V of block k-1, which was relative to the old max
 #pragma unroll
