@@ -81,6 +81,10 @@ constexpr int kBr = kRowsPerWave * kWaves;  // query rows per workgroup
 constexpr int kBc = 64;                     // keys per K/V tile (two 32-key blocks)
 constexpr int kXcds = 8;                    // MI355X: 8 XCDs, workgroups dealt round-robin
 constexpr float kNegInf = -__builtin_inff();
+// A block's probabilities are taken against a reference max that may lag
+// the true running max by up to kRefSlack (log2 units): p <= 2^16.  A row
+// whose next block would exceed that moves the reference to its exact max.
+constexpr float kRefSlack = 16.f;
 // Buffer-resource word 3 for raw (unformatted, stride-0) 32-bit loads with
 // out-of-range offsets returning zero.
 constexpr int kBufferFlags = 0x00020000;
@@ -102,10 +106,11 @@ struct Tile {
 //  chunk): D = 128 uses a 4-bit swizzle, distinct over any 16 consecutive
 //  rows; D = 64 (8 chunks, two rows per 256 bytes) uses one distinct over
 //  any aligned 8 rows and over (row parity, position) for 16 rows.
-//  V tiles (read by ds_read_b64_tr_b16, 16 lanes on 4 aligned rows x 2
-//  adjacent chunks {2u, 2u+1}): a 3-bit swizzle whose pairs are distinct
-//  over any 4 aligned rows; it leaves chunk bit 3 alone, so head-dim blocks
-//  64 apart are a fixed 128 bytes apart.
+//  V tiles (read by ds_read_b64_tr_b16; the LDS serves 32 lanes per cycle:
+//  4 aligned rows x the 4 chunks of one 32-column head-dim block): D = 128
+//  (one row per 256 bytes) XORs (r & 3) into chunk bits 2..3, so the 4 rows
+//  land on 4 distinct 64-byte bank blocks; D = 64 (two rows per 256 bytes)
+//  needs rows r and r+2 apart, which bit 2 = (r >> 1) & 1 gives.
 template <int D>
 __device__ __forceinline__ int swz_k(int r)
 {
@@ -115,7 +120,14 @@ __device__ __forceinline__ int swz_k(int r)
         return (r & 7) ^ ((r >> 3) & 1);
 }
 
-__device__ __forceinline__ int swz_v(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+template <int D>
+__device__ __forceinline__ int swz_v(int r)
+{
+    if constexpr (D == 128)
+        return (r & 3) << 2;
+    else
+        return ((r & 3) << 1) | ((r >> 2) & 1);
+}
 
 template <int D>
 __device__ __forceinline__ int k_offset(int r, int c)
@@ -126,7 +138,7 @@ __device__ __forceinline__ int k_offset(int r, int c)
 template <int D>
 __device__ __forceinline__ int v_offset(int r, int c)
 {
-    return r * Tile<D>::kRowBytes + ((c ^ swz_v(r)) << 4);
+    return r * Tile<D>::kRowBytes + ((c ^ swz_v<D>(r)) << 4);
 }
 
 // v_permlane32_swap_b32 a, b exchanges lanes 32..63 of a with lanes 0..31 of
@@ -226,7 +238,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
         const int r = slice * T::kRowsPerLoad + lane / T::kChunks;
         const int pos = lane % T::kChunks;
         kdma[i] = r * T::kRowBytes + ((pos ^ swz_k<D>(r)) << 4);
-        vdma[i] = r * T::kRowBytes + ((pos ^ swz_v(r)) << 4);
+        vdma[i] = r * T::kRowBytes + ((pos ^ swz_v<D>(r)) << 4);
     }
     // K operand of S^T = K Q^T: row n of a 32-key block, chunk 2 st + half.
     uint32_t koff[T::kQkSteps];
@@ -235,13 +247,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
         koff[st] = k_offset<D>(n, 2 * st + half);
     // V^T operand through ds_read_b64_tr_b16: source lane i of 16-lane group
     // g reads key row 8 jj + 4 (g / 2) + i / 4 of a 16-key step, head-dim
-    // columns 32 b + 16 (g % 2) + 4 (i % 4) .. +3.  Blocks b and b+2 are 128
-    // bytes apart (the V swizzle keeps chunk bit 3).
-    uint32_t voff[2][2];
+    // columns 32 b + 16 (g % 2) + 4 (i % 4) .. +3.
+    uint32_t voff[T::kOBlocks][2];
     {
         const int g = lane >> 4, i = lane & 15;
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < T::kOBlocks; ++b)
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
                 const int r = 8 * jj + 4 * (g >> 1) + (i >> 2);
@@ -251,7 +262,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     }
     auto vread = [&](const char *buf, int byte, int b, int jj) __attribute__((always_inline)) {  // 4 keys x 1 head-dim column, transposed
         return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            LDS_PTR(s16x4, buf + byte + 128 * (b >> 1) + voff[b & 1][jj]));
+            LDS_PTR(s16x4, buf + byte + voff[b][jj]));
     };
 
     // One K or V tile (64 keys from kv0) into an LDS buffer: this wave's
@@ -300,9 +311,34 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
 #pragma unroll
     for (int b = 0; b < T::kOBlocks; ++b)
         oacc[b] = f32x16{};
-    float m_ref = kNegInf;  // running max, log2 units (scores times c_log2)
-    float l_run = 0.f;      // running sum over this lane's half of the keys
+    // Key r of block kb (register r of the score tile) is visible to this
+    // lane's query: inside the sequence and, causal, not after the query.
+    auto visible = [&](int kb, int r) __attribute__((always_inline)) {
+        const int key = 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
+        return !(key >= N || (CAUSAL && key > qidx));
+    };
+    // Reference max m_ref of this lane's row (log2 units, scores times
+    // c_log2), the value subtracted before exp2 (m_ref, or 0 while nothing
+    // is visible) and the largest score the reference still serves.
+    float m_ref, m_sub, m_thr;
+    auto set_ref = [&](float m) __attribute__((always_inline)) {
+        m_ref = m;
+        m_sub = (m == kNegInf) ? 0.f : m;
+        m_thr = m + kRefSlack;
+    };
+    {  // block 0 sets the first reference: its exact row max
+        float mx = kNegInf;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            mx = fmaxf(mx, visible(0, r) ? sc[r] * c_log2 : kNegInf);
+        set_ref(wave_half_max(mx));
+    }
+    float l_run = 0.f;       // sum of fp32 p over this lane's half of the keys
+    float lb_run = 0.f;      // sum of the bf16-rounded p, same keys
+    bool pending = false;    // O still to be rescaled by alpha_pend (wave-uniform)
+    float alpha_pend = 1.f;
     bf16x8 pb_prev[2] = {bf16x8{}, bf16x8{}};  // P of the previous block (none yet: zeros)
+    const bf16x2 kOnes = __builtin_bit_cast(bf16x2, 0x3f803f80u);  // bf16 {1, 1}
 
     // O^T += V^T P^T over the 32 keys of one block (two 16-key k-steps);
     // the block's first V row is at byte vp of V buffer vbuf.
@@ -326,12 +362,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     // from byte kq of buffer kbuf) and P V of block k-1 (V rows from byte vp of
     // buffer vbuf).  The first step multiplies the zeroed V buffer by P = 0;
     // the last computes scores of a block that does not exist and discards
-    // them.  MASKED steps apply the causal / sequence-end mask and also serve
-    // non-positive scales.  LOADS steps also copy K tile load_t+1 into kdst
-    // and V tile load_t into vdst, spread among their MFMAs.
-    auto step = [&](int k, const char *kbuf, int kq, const char *vbuf, int vp, auto masked_tag, auto loads_tag,
-                    int load_t, char *kdst, char *vdst) __attribute__((always_inline)) {
+    // them.  MASKED steps apply the causal / sequence-end mask.  LOADS steps
+    // also copy K tile load_t+1 into kdst and V tile load_t into vdst, spread
+    // among their MFMAs.
+    auto step = [&](int k, const char *kbuf, int kq, const char *vbuf, int vp, auto masked_tag,
+                    auto next_masked_tag, auto loads_tag, int load_t, char *kdst, char *vdst) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked_tag)::value;
+        constexpr bool NEXT_MASKED = decltype(next_masked_tag)::value;
         constexpr bool LOADS = decltype(loads_tag)::value;
         // Keep the per-lane LDS offsets opaque inside the loop: otherwise
         // their sums with each buffer's constant base are hoisted out of the
@@ -340,62 +377,53 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
 #pragma unroll
         for (int st = 0; st < T::kQkSteps; ++st)
             asm volatile("" : "+v"(koff[st]));
-        asm volatile("" : "+v"(voff[0][0]), "+v"(voff[0][1]), "+v"(voff[1][0]), "+v"(voff[1][1]));
+#pragma unroll
+        for (int b = 0; b < T::kOBlocks; ++b)
+            asm volatile("" : "+v"(voff[b][0]), "+v"(voff[b][1]));
         // Pin the softmax inside its step: without this, loop rotation moves
         // the first step's VALU work into the previous iteration's latch, away
         // from the MFMAs it is meant to overlap.
         asm volatile("" : "+v"(sc));
 
-        // Register 4j+e holds key 32 k + 8 j + 4 half + e.
-        float mx;
-        if constexpr (!MASKED) {
-            float r0 = sc[0];
-#pragma unroll
-            for (int r = 1; r < 16; ++r)
-                r0 = fmaxf(r0, sc[r]);
-            mx = r0 * c_log2;
-        } else {
-            mx = kNegInf;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float x = sc[r] * c_log2;
-                const int key = 32 * k + 8 * (r >> 2) + 4 * half + (r & 3);
-                x = (key >= N || (CAUSAL && key > qidx)) ? kNegInf : x;
-                sc[r] = x;
-                mx = fmaxf(mx, x);
-            }
-        }
-        mx = wave_half_max(mx);
-
-        // Exact running max; O needs rescaling only if some row of the wave
-        // found a new max in this block (always so on the first block).
-        const float m_new = fmaxf(m_ref, mx);
-        const bool rescale = __builtin_amdgcn_ballot_w64(m_new > m_ref) != 0;  // wave-uniform
-        const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-        m_ref = m_new;
-        const float m_use = (m_ref == kNegInf) ? 0.f : m_ref;  // all masked so far: p = 0, no NaN
-        // Unmasked blocks hold raw scores (p = exp2(s c - m)); masked ones hold s c already.
-        const float cmul = MASKED ? 1.f : c_log2;
-
+        // Register 4j+e holds key 32 k + 8 j + 4 half + e.  This block's P
+        // is taken against m_sub (the reference max, log2 units), fixed
+        // before the step, so the exps need nothing from this block's max:
+        // the previous step checked that every visible p stays <= 2^kRefSlack.
+        // l sums the fp32 p (for the LSE), lb the bf16-rounded p that P V
+        // actually multiplies (for O).
         float p[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-            p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], cmul, -m_use));
-        // l sums fp32 p, before the bf16 rounding used by P V (two chains).
+        for (int r = 0; r < 16; ++r) {
+            p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], c_log2, -m_sub));
+            if constexpr (MASKED)
+                p[r] = visible(k, r) ? p[r] : 0.f;
+        }
         float rs0 = p[0], rs1 = p[1];
 #pragma unroll
         for (int r = 2; r < 16; r += 2) {
             rs0 += p[r];
             rs1 += p[r + 1];
         }
-        const float rowsum = rs0 + rs1;
+        // The bf16 pairs are summed from the scalar words: summing from the
+        // elements of the packed vector (w[e] in a loop) gets all four dot
+        // products fed the first element by the compiler.
         bf16x8 pb[2];
+        float rb0 = 0.f, rb1 = 0.f;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            const u32x4 w = {pack_bf16x2(p[8 * ks + 0], p[8 * ks + 1]), pack_bf16x2(p[8 * ks + 2], p[8 * ks + 3]),
-                             pack_bf16x2(p[8 * ks + 4], p[8 * ks + 5]), pack_bf16x2(p[8 * ks + 6], p[8 * ks + 7])};
+            const uint32_t w0 = pack_bf16x2(p[8 * ks + 0], p[8 * ks + 1]);
+            const uint32_t w1 = pack_bf16x2(p[8 * ks + 2], p[8 * ks + 3]);
+            const uint32_t w2 = pack_bf16x2(p[8 * ks + 4], p[8 * ks + 5]);
+            const uint32_t w3 = pack_bf16x2(p[8 * ks + 6], p[8 * ks + 7]);
+            rb0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), kOnes, rb0, false);
+            rb1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), kOnes, rb1, false);
+            rb0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), kOnes, rb0, false);
+            rb1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), kOnes, rb1, false);
+            const u32x4 w = {w0, w1, w2, w3};
             pb[ks] = __builtin_bit_cast(bf16x8, w);
         }
+        l_run += rs0 + rs1;
+        lb_run += rb0 + rb1;
 
         if constexpr (LOADS) {
             load_tile(Kh, (load_t + 1) * kBc, kdst, kdma);
@@ -407,8 +435,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
             sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*LDS_PTR(const bf16x8, kbuf + kq + koff[st]), qop[st],
                                                          sn, 0, 0, 0);
         pv(vbuf, vp, pb_prev);
-        sc = sn;
-        l_run = alpha * l_run + rowsum;
+
+        // Row max of the next block (this lane's half of its keys, log2
+        // units), for the next step's reference.
+        float mx;
+        if constexpr (NEXT_MASKED) {
+            mx = kNegInf;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                mx = fmaxf(mx, visible(k + 1, r) ? sn[r] * c_log2 : kNegInf);
+        } else {  // every key visible and c_log2 > 0
+            float r0 = sn[0];
+#pragma unroll
+            for (int r = 1; r < 16; ++r)
+                r0 = fmaxf(r0, sn[r]);
+            mx = r0 * c_log2;
+        }
+        const bool reref = __builtin_amdgcn_ballot_w64(mx > m_thr) != 0;  // wave-uniform
 
         // Issue order for this step's scheduling region: the 16 MFMAs (8 for
         // the next scores, 8 for P V) each followed by a share of the softmax
@@ -420,22 +463,36 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
 #pragma unroll
         for (int i = 0; i < 2 * T::kQkSteps; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);  // VALU incl. transcendental
+            __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);  // VALU incl. transcendental
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
             if (LOADS && i < 2 * T::kLoadsPerWave)
                 __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // tile copy (VMEM)
         }
-
-        // Keep this block's P and row sum inside this step: otherwise the
+        // Keep this block's P and row sums inside this step: otherwise the
         // compiler sinks the exps and adds next to their first uses (the next
         // step's P V and the loop latch), where no MFMA is left to hide them.
-        asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(l_run));
+        asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(l_run), "+v"(lb_run));
 
-        if (rescale) {  // after P V of block k-1, which was relative to the old max
+        // The reference moved at the previous step: O now holds P V of block
+        // k-1 as well, taken against the old reference, so rescale it here.
+        if (pending) {
 #pragma unroll
             for (int b = 0; b < T::kOBlocks; ++b)
-                oacc[b] *= alpha;
+                oacc[b] *= alpha_pend;
         }
+        // Some row of the next block has a p above 2^kRefSlack against the
+        // current reference: move the reference to the row's exact running
+        // max (both halves of the row) and rescale the sums now, O after the
+        // next P V.
+        pending = reref;
+        if (reref) {
+            const float m_new = fmaxf(m_ref, wave_half_max(mx));
+            alpha_pend = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+            l_run *= alpha_pend;
+            lb_run *= alpha_pend;
+            set_ref(m_new);
+        }
+        sc = sn;
         pb_prev[0] = pb[0];
         pb_prev[1] = pb[1];
     };
@@ -445,46 +502,65 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     // after the barrier the odd step refills those buffers with K tile t+2 and
     // V tile t+1 (past the end: zeros, no memory traffic), which land before
     // the next barrier.
-    auto tile = [&](int t, auto parity_tag, auto masked_tag) __attribute__((always_inline)) {
+    // NEXT_MASKED: whether the block after the tile (the first of tile t+1)
+    // needs the mask.
+    auto tile = [&](int t, auto parity_tag, auto masked_tag, auto next_masked_tag) __attribute__((always_inline)) {
         constexpr int P = decltype(parity_tag)::value;
         constexpr int kHalf = 32 * T::kRowBytes;
         char *kp = P ? sk1 : sk0, *kq = P ? sk0 : sk1;
         char *vp = P ? sv1 : sv0, *vq = P ? sv0 : sv1;
-        step(2 * t, kp, kHalf, vq, kHalf, masked_tag, std::false_type{}, 0, kp, vq);
+        step(2 * t, kp, kHalf, vq, kHalf, masked_tag, masked_tag, std::false_type{}, 0, kp, vq);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        step(2 * t + 1, kq, 0, vp, 0, masked_tag, std::true_type{}, t + 1, kp, vq);
+        step(2 * t + 1, kq, 0, vp, 0, masked_tag, next_masked_tag, std::true_type{}, t + 1, kp, vq);
     };
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
+    using Unmasked = std::false_type;
+    using Masked = std::true_type;
 
     // Tiles [0, t_free) need no mask: below the causal diagonal of every
-    // query of the workgroup and wholly inside the sequence.  t_free is made
-    // even so that both loops walk (buffer 0, buffer 1) tile pairs.
+    // query of the workgroup and wholly inside the sequence (and a positive
+    // scale, which the unmasked row max assumes).  t_free is made even so
+    // that the loops walk (buffer 0, buffer 1) tile pairs; the last unmasked
+    // pair is peeled because the block after it needs the mask.
     int t_free = N / kBc;
     if (CAUSAL)
         t_free = min(t_free, (q0 + 1) / kBc);
     if (!(c_log2 > 0.f))
         t_free = 0;
     t_free = min(t_free, ntiles) & ~1;
-    for (int t = 0; t < t_free; t += 2) {
-        tile(t, P0{}, std::false_type{});
-        tile(t + 1, P1{}, std::false_type{});
+    int t = 0;
+    for (; t + 2 < t_free; t += 2) {
+        tile(t, P0{}, Unmasked{}, Unmasked{});
+        tile(t + 1, P1{}, Unmasked{}, Unmasked{});
     }
-    for (int t = t_free; t < ntiles; t += 2) {
-        tile(t, P0{}, std::true_type{});
+    if (t < t_free) {
+        tile(t, P0{}, Unmasked{}, Unmasked{});
+        tile(t + 1, P1{}, Unmasked{}, Masked{});
+        t += 2;
+    }
+    for (; t < ntiles; t += 2) {
+        tile(t, P0{}, Masked{}, Masked{});
         if (t + 1 < ntiles)
-            tile(t + 1, P1{}, std::true_type{});
+            tile(t + 1, P1{}, Masked{}, Masked{});
     }
     // P V of the last block: second half of V tile ntiles-1.
     pv((ntiles - 1) & 1 ? sv1 : sv0, 32 * T::kRowBytes, pb_prev);
+    if (pending) {
+#pragma unroll
+        for (int b = 0; b < T::kOBlocks; ++b)
+            oacc[b] *= alpha_pend;
+    }
     __builtin_amdgcn_s_waitcnt(0);  // no copy may still be writing LDS when the workgroup ends
 
-    // Epilogue: O = O / l, LSE = ln2 * (m + log2 l).
+    // Epilogue: O = O / lb (the sum of the bf16 weights that built O),
+    // LSE = ln2 * (m + log2 l) from the fp32 sum.
     const float l_tot = wave_half_sum(l_run);
+    const float lb_tot = wave_half_sum(lb_run);
     if (!q_ok)
         return;
-    const float inv = 1.f / l_tot;
+    const float inv = 1.f / lb_tot;
     __bf16 *orow = O + head + (size_t)qidx * D;
 #pragma unroll
     for (int b = 0; b < T::kOBlocks; ++b) {
