@@ -1,7 +1,7 @@
 // attn_fwd_kernel.hip -- fused exact attention forward pass for gfx950.
 //
-// One workgroup owns one (batch*head, query tile) pair and walks the key/value
-// tiles of that head in order (the FlashAttention-2 loop order and sequence
+// A workgroup owns a query tile of one batch*head (two, in turn, under the
+// causal mask) and walks the key/value tiles of that head in order (the FlashAttention-2 loop order and sequence
 // parallelism: "FlashAttention 1-4 evolution cheat sheet", argus-lessons,
 // FlashAttention-2 section).  Per key/value block it forms the score tile on
 // the matrix cores, keeps a running row max m and running sum l, rescales the
@@ -40,19 +40,26 @@
 //     reads.  K is prefetched two 64-key tiles ahead and V one tile ahead,
 //     double-buffered, one barrier per tile.
 //   * exp is v_exp_f32 (base 2) with scale*log2(e) folded into one FMA.
-//     The row max is exact at every 32-key block, so the largest probability
-//     of a row is exactly 1 and rounds to bf16 without error; the O rescale
-//     is skipped (a wave-uniform branch) when no row of the wave found a new
-//     max.  (A reference max that lags by up to 2^8, as in the conditional
-//     rescaling of the FlashAttention-4 section, leaves the dominant
-//     probability inexact in bf16 and breaks the 1e-2 bound on large-logit
-//     inputs.)
+//     Probabilities are taken against a reference max that may lag the
+//     exact running max by up to 16 (log2 units), the conditional rescaling
+//     of the FlashAttention-4 section of the cheat sheet: the exps of a block
+//     never wait for its own max.  Each step computes the row max of the
+//     NEXT block from its fresh scores (during the P V MFMAs); a row that
+//     would pass the slack moves the reference to its exact max, a rare
+//     wave-uniform branch that rescales the sums at once and O after the
+//     next P V.  With a lagging reference the largest p is not 1 and its
+//     bf16 rounding is not exact, so O is divided by the sum of the
+//     bf16-rounded probabilities that built it (v_dot2c_f32_bf16 against
+//     ones), which keeps a one-hot row exact; the LSE uses the fp32 sum.
 //   * Causal: tiles entirely above the diagonal are never loaded; the mask
 //     is applied only in tiles that cross the diagonal or the sequence end.
-//   * Workgroup order: heaviest causal query tiles first (longest-processing-
-//     time order, FlashAttention-4 section of the cheat sheet), and the tiles
-//     of one head kept on one XCD so that its K/V stream is shared through
-//     that XCD's L2.
+//   * Causal load balance: a workgroup runs two query tiles of one head in
+//     turn, tile nqt-1-j and then tile j, so every workgroup walks nearly the
+//     same number of key tiles and the launch ends without a tail of heavy
+//     diagonal-far tiles (the balancing concern of the FlashAttention-4
+//     section of the cheat sheet, met here by pairing instead of ordering).
+//     Workgroups of one head stay on one XCD so that its K/V stream is shared
+//     through that XCD's L2.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -175,17 +182,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 }
 
 // Logical workgroup order: XCD-major (consecutive logical indices share an
-// XCD), then head-major, then query tiles from the last (heaviest under the
-// causal mask) to the first.
-__device__ __forceinline__ void tile_of(int wg, int n_wg, int nqt, int &bh, int &qt)
+// XCD, so the units of one head stay on one XCD), then head-major.
+__device__ __forceinline__ void unit_of(int wg, int n_wg, int n_units, int &bh, int &unit)
 {
     const int xcd = wg % kXcds;
     const int slot = wg / kXcds;
     const int per = n_wg / kXcds;
     const int extra = n_wg % kXcds;
     const int lin = xcd * per + (xcd < extra ? xcd : extra) + slot;
-    bh = lin / nqt;
-    qt = nqt - 1 - lin % nqt;
+    bh = lin / n_units;
+    unit = lin % n_units;
 }
 
 template <int D, bool CAUSAL>
@@ -211,369 +217,379 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
     const int n = lane & 31;     // this lane's query column in the 32x32 tiles
     const int half = lane >> 5;  // which half of the 32 keys / 16 k-values
 
-    int bh, qt;
-    tile_of(blockIdx.x, n_wg, nqt, bh, qt);
-    const int q0 = qt * kBr;
-    const size_t head = (size_t)bh * (size_t)N * D;
-    // Copies go through buffer resources over this head's K and V: offsets at
-    // or past N rows are out of range and read as zeros.
-    const int head_bytes = N * T::kRowBytes;
-    const __bf16 *Kh = K + head;
-    const __bf16 *Vh = V + head;
+    // Causal: unit j of a head is the pair of query tiles (nqt-1-j, j), the
+    // heavy one first, so that every workgroup does nearly the same work (the
+    // middle tile of an odd count is alone); non-causal: one tile per unit.
+    const int n_units = CAUSAL ? (nqt + 1) / 2 : nqt;
+    int bh, unit;
+    unit_of(blockIdx.x, n_wg, n_units, bh, unit);
+    const int npass = (CAUSAL && nqt - 1 - unit != unit) ? 2 : 1;
+    for (int pass = 0; pass < npass; ++pass) {
+        const int qt = CAUSAL ? (pass == 0 ? nqt - 1 - unit : unit) : unit;
+        if (pass > 0)
+            __syncthreads();  // every wave is done with the previous tile's LDS
+        const int q0 = qt * kBr;
+        const size_t head = (size_t)bh * (size_t)N * D;
+        // Copies go through buffer resources over this head's K and V: offsets at
+        // or past N rows are out of range and read as zeros.
+        const int head_bytes = N * T::kRowBytes;
+        const __bf16 *Kh = K + head;
+        const __bf16 *Vh = V + head;
 
-    const int qw0 = q0 + wave * kRowsPerWave;  // first query of this wave
-    const int qidx = qw0 + n;
-    const bool q_ok = qidx < N;
+        const int qw0 = q0 + wave * kRowsPerWave;  // first query of this wave
+        const int qidx = qw0 + n;
+        const bool q_ok = qidx < N;
 
-    const int kv_end = CAUSAL ? min(N, q0 + kBr) : N;
-    const int ntiles = (kv_end + kBc - 1) / kBc;
+        const int kv_end = CAUSAL ? min(N, q0 + kBr) : N;
+        const int ntiles = (kv_end + kBc - 1) / kBc;
 
-    // ---- per-lane offsets, fixed for the whole loop ----
-    // DMA: slice i of this wave is LDS bytes [1024 s, 1024 s + 1024) of a tile
-    // (s = wave * kLoadsPerWave + i); the lane fetches row r, chunk c.
-    uint32_t kdma[T::kLoadsPerWave], vdma[T::kLoadsPerWave];
+        // ---- per-lane offsets, fixed for the whole loop ----
+        // DMA: slice i of this wave is LDS bytes [1024 s, 1024 s + 1024) of a tile
+        // (s = wave * kLoadsPerWave + i); the lane fetches row r, chunk c.
+        uint32_t kdma[T::kLoadsPerWave], vdma[T::kLoadsPerWave];
 #pragma unroll
-    for (int i = 0; i < T::kLoadsPerWave; ++i) {
-        const int slice = wave * T::kLoadsPerWave + i;
-        const int r = slice * T::kRowsPerLoad + lane / T::kChunks;
-        const int pos = lane % T::kChunks;
-        kdma[i] = r * T::kRowBytes + ((pos ^ swz_k<D>(r)) << 4);
-        vdma[i] = r * T::kRowBytes + ((pos ^ swz_v<D>(r)) << 4);
-    }
-    // K operand of S^T = K Q^T: row n of a 32-key block, chunk 2 st + half.
-    uint32_t koff[T::kQkSteps];
-#pragma unroll
-    for (int st = 0; st < T::kQkSteps; ++st)
-        koff[st] = k_offset<D>(n, 2 * st + half);
-    // V^T operand through ds_read_b64_tr_b16: source lane i of 16-lane group
-    // g reads key row 8 jj + 4 (g / 2) + i / 4 of a 16-key step, head-dim
-    // columns 32 b + 16 (g % 2) + 4 (i % 4) .. +3.
-    uint32_t voff[T::kOBlocks][2];
-    {
-        const int g = lane >> 4, i = lane & 15;
-#pragma unroll
-        for (int b = 0; b < T::kOBlocks; ++b)
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                const int r = 8 * jj + 4 * (g >> 1) + (i >> 2);
-                const int dcol = 32 * b + 16 * (g & 1) + 4 * (i & 3);
-                voff[b][jj] = v_offset<D>(r, dcol >> 3) + ((dcol & 4) << 1);
-            }
-    }
-    auto vread = [&](const char *buf, int byte, int b, int jj) __attribute__((always_inline)) {  // 4 keys x 1 head-dim column, transposed
-        return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            LDS_PTR(s16x4, buf + byte + voff[b][jj]));
-    };
-
-    // One K or V tile (64 keys from kv0) into an LDS buffer: this wave's
-    // kLoadsPerWave 1 KB slices, each one buffer_load_dwordx4 ... lds.  Rows
-    // past N, and whole tiles past the end, read as zeros (no memory access),
-    // so the copy needs no branch.
-    auto load_tile = [&](const __bf16 *src, int kv0, char *buf, const uint32_t *dma) __attribute__((always_inline)) {
-        const __amdgpu_buffer_rsrc_t rsrc =
-            __builtin_amdgcn_make_buffer_rsrc((void *)src, (short)0, head_bytes, kBufferFlags);
-#pragma unroll
-        for (int i = 0; i < T::kLoadsPerWave; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rsrc, LDS_PTR(void, buf + (wave_u * T::kLoadsPerWave + i) * 1024), 16, dma[i],
-                kv0 * T::kRowBytes, 0, 0);
-    };
-
-    // Prologue: K tiles 0 and 1 and V tile 0 in flight while Q is read; V
-    // buffer 1 is zeroed for the first step's (empty) P V.
-    load_tile(Kh, 0, sk0, kdma);
-    load_tile(Kh, kBc, sk1, kdma);
-    load_tile(Vh, 0, sv0, vdma);
-#pragma unroll
-    for (int i = 0; i < T::kBytes / (16 * kThreads); ++i)
-        *LDS_PTR(u32x4, sv1 + 16 * (tid + i * kThreads)) = u32x4{};
-
-    // Q^T operand, resident for the whole key loop: k-step s holds
-    // q[qidx][16 s + 8 half .. +7] (zeros past N).
-    bf16x8 qop[T::kQkSteps];
-    {
-        const __bf16 *qrow = Q + head + (size_t)min(qidx, N - 1) * D + 8 * half;
-#pragma unroll
-        for (int s = 0; s < T::kQkSteps; ++s) {
-            qop[s] = *reinterpret_cast<const bf16x8 *>(qrow + 16 * s);
-            if (!q_ok)
-                qop[s] = bf16x8{};
+        for (int i = 0; i < T::kLoadsPerWave; ++i) {
+            const int slice = wave * T::kLoadsPerWave + i;
+            const int r = slice * T::kRowsPerLoad + lane / T::kChunks;
+            const int pos = lane % T::kChunks;
+            kdma[i] = r * T::kRowBytes + ((pos ^ swz_k<D>(r)) << 4);
+            vdma[i] = r * T::kRowBytes + ((pos ^ swz_v<D>(r)) << 4);
         }
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
-    f32x16 sc = {};  // scores of the block being turned into probabilities
-#pragma unroll
-    for (int st = 0; st < T::kQkSteps; ++st)
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*LDS_PTR(const bf16x8, sk0 + koff[st]), qop[st], sc, 0, 0, 0);
-    f32x16 oacc[T::kOBlocks];
-#pragma unroll
-    for (int b = 0; b < T::kOBlocks; ++b)
-        oacc[b] = f32x16{};
-    // Key r of block kb (register r of the score tile) is visible to this
-    // lane's query: inside the sequence and, causal, not after the query.
-    auto visible = [&](int kb, int r) __attribute__((always_inline)) {
-        const int key = 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-        return !(key >= N || (CAUSAL && key > qidx));
-    };
-    // Reference max m_ref of this lane's row (log2 units, scores times
-    // c_log2), the value subtracted before exp2 (m_ref, or 0 while nothing
-    // is visible) and the largest score the reference still serves.
-    float m_ref, m_sub, m_thr;
-    auto set_ref = [&](float m) __attribute__((always_inline)) {
-        m_ref = m;
-        m_sub = (m == kNegInf) ? 0.f : m;
-        m_thr = m + kRefSlack;
-    };
-    {  // block 0 sets the first reference: its exact row max
-        float mx = kNegInf;
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            mx = fmaxf(mx, visible(0, r) ? sc[r] * c_log2 : kNegInf);
-        set_ref(wave_half_max(mx));
-    }
-    float l_run = 0.f;       // sum of fp32 p over this lane's half of the keys
-    float lb_run = 0.f;      // sum of the bf16-rounded p, same keys
-    bool pending = false;    // O still to be rescaled by alpha_pend (wave-uniform)
-    float alpha_pend = 1.f;
-    bf16x8 pb_prev[2] = {bf16x8{}, bf16x8{}};  // P of the previous block (none yet: zeros)
-    const bf16x2 kOnes = __builtin_bit_cast(bf16x2, 0x3f803f80u);  // bf16 {1, 1}
-
-    // O^T += V^T P^T over the 32 keys of one block (two 16-key k-steps);
-    // the block's first V row is at byte vp of V buffer vbuf.
-    auto pv = [&](const char *vbuf, int vp, const bf16x8 *pbk) __attribute__((always_inline)) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-            for (int b = 0; b < T::kOBlocks; ++b) {
-                const int vb = vp + ks * 16 * T::kRowBytes;
-                const u32x2 lo = __builtin_bit_cast(u32x2, vread(vbuf, vb, b, 0));
-                const u32x2 hi = __builtin_bit_cast(u32x2, vread(vbuf, vb, b, 1));
-                const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
-                oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va), pbk[ks], oacc[b],
-                                                                  0, 0, 0);
-            }
-        }
-    };
-
-    // One 32-key pipeline step (block k): the softmax of block k on the VALU
-    // interleaves with the matrix-core work of the scores of block k+1 (K rows
-    // from byte kq of buffer kbuf) and P V of block k-1 (V rows from byte vp of
-    // buffer vbuf).  The first step multiplies the zeroed V buffer by P = 0;
-    // the last computes scores of a block that does not exist and discards
-    // them.  MASKED steps apply the causal / sequence-end mask.  LOADS steps
-    // also copy K tile load_t+1 into kdst and V tile load_t into vdst, spread
-    // among their MFMAs.
-    auto step = [&](int k, const char *kbuf, int kq, const char *vbuf, int vp, auto masked_tag,
-                    auto next_masked_tag, auto loads_tag, int load_t, char *kdst, char *vdst) __attribute__((always_inline)) {
-        constexpr bool MASKED = decltype(masked_tag)::value;
-        constexpr bool NEXT_MASKED = decltype(next_masked_tag)::value;
-        constexpr bool LOADS = decltype(loads_tag)::value;
-        // Keep the per-lane LDS offsets opaque inside the loop: otherwise
-        // their sums with each buffer's constant base are hoisted out of the
-        // loop as separate registers instead of riding in the ds_read
-        // immediate offset field.
+        // K operand of S^T = K Q^T: row n of a 32-key block, chunk 2 st + half.
+        uint32_t koff[T::kQkSteps];
 #pragma unroll
         for (int st = 0; st < T::kQkSteps; ++st)
-            asm volatile("" : "+v"(koff[st]));
+            koff[st] = k_offset<D>(n, 2 * st + half);
+        // V^T operand through ds_read_b64_tr_b16: source lane i of 16-lane group
+        // g reads key row 8 jj + 4 (g / 2) + i / 4 of a 16-key step, head-dim
+        // columns 32 b + 16 (g % 2) + 4 (i % 4) .. +3.
+        uint32_t voff[T::kOBlocks][2];
+        {
+            const int g = lane >> 4, i = lane & 15;
 #pragma unroll
-        for (int b = 0; b < T::kOBlocks; ++b)
-            asm volatile("" : "+v"(voff[b][0]), "+v"(voff[b][1]));
-        // Pin the softmax inside its step: without this, loop rotation moves
-        // the first step's VALU work into the previous iteration's latch, away
-        // from the MFMAs it is meant to overlap.
-        asm volatile("" : "+v"(sc));
+            for (int b = 0; b < T::kOBlocks; ++b)
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+                    const int r = 8 * jj + 4 * (g >> 1) + (i >> 2);
+                    const int dcol = 32 * b + 16 * (g & 1) + 4 * (i & 3);
+                    voff[b][jj] = v_offset<D>(r, dcol >> 3) + ((dcol & 4) << 1);
+                }
+        }
+        auto vread = [&](const char *buf, int byte, int b, int jj) __attribute__((always_inline)) {  // 4 keys x 1 head-dim column, transposed
+            return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                LDS_PTR(s16x4, buf + byte + voff[b][jj]));
+        };
 
-        // Register 4j+e holds key 32 k + 8 j + 4 half + e.  This block's P
-        // is taken against m_sub (the reference max, log2 units), fixed
-        // before the step, so the exps need nothing from this block's max:
-        // the previous step checked that every visible p stays <= 2^kRefSlack.
-        // l sums the fp32 p (for the LSE), lb the bf16-rounded p that P V
-        // actually multiplies (for O).
-        float p[16];
+        // One K or V tile (64 keys from kv0) into an LDS buffer: this wave's
+        // kLoadsPerWave 1 KB slices, each one buffer_load_dwordx4 ... lds.  Rows
+        // past N, and whole tiles past the end, read as zeros (no memory access),
+        // so the copy needs no branch.
+        auto load_tile = [&](const __bf16 *src, int kv0, char *buf, const uint32_t *dma) __attribute__((always_inline)) {
+            const __amdgpu_buffer_rsrc_t rsrc =
+                __builtin_amdgcn_make_buffer_rsrc((void *)src, (short)0, head_bytes, kBufferFlags);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], c_log2, -m_sub));
-            if constexpr (MASKED)
-                p[r] = visible(k, r) ? p[r] : 0.f;
-        }
-        float rs0 = p[0], rs1 = p[1];
-#pragma unroll
-        for (int r = 2; r < 16; r += 2) {
-            rs0 += p[r];
-            rs1 += p[r + 1];
-        }
-        // The bf16 pairs are summed from the scalar words: summing from the
-        // elements of the packed vector (w[e] in a loop) gets all four dot
-        // products fed the first element by the compiler.
-        bf16x8 pb[2];
-        float rb0 = 0.f, rb1 = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const uint32_t w0 = pack_bf16x2(p[8 * ks + 0], p[8 * ks + 1]);
-            const uint32_t w1 = pack_bf16x2(p[8 * ks + 2], p[8 * ks + 3]);
-            const uint32_t w2 = pack_bf16x2(p[8 * ks + 4], p[8 * ks + 5]);
-            const uint32_t w3 = pack_bf16x2(p[8 * ks + 6], p[8 * ks + 7]);
-            rb0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), kOnes, rb0, false);
-            rb1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), kOnes, rb1, false);
-            rb0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), kOnes, rb0, false);
-            rb1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), kOnes, rb1, false);
-            const u32x4 w = {w0, w1, w2, w3};
-            pb[ks] = __builtin_bit_cast(bf16x8, w);
-        }
-        l_run += rs0 + rs1;
-        lb_run += rb0 + rb1;
+            for (int i = 0; i < T::kLoadsPerWave; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rsrc, LDS_PTR(void, buf + (wave_u * T::kLoadsPerWave + i) * 1024), 16, dma[i],
+                    kv0 * T::kRowBytes, 0, 0);
+        };
 
-        if constexpr (LOADS) {
-            load_tile(Kh, (load_t + 1) * kBc, kdst, kdma);
-            load_tile(Vh, load_t * kBc, vdst, vdma);
+        // Prologue: K tiles 0 and 1 and V tile 0 in flight while Q is read; V
+        // buffer 1 is zeroed for the first step's (empty) P V.
+        load_tile(Kh, 0, sk0, kdma);
+        load_tile(Kh, kBc, sk1, kdma);
+        load_tile(Vh, 0, sv0, vdma);
+#pragma unroll
+        for (int i = 0; i < T::kBytes / (16 * kThreads); ++i)
+            *LDS_PTR(u32x4, sv1 + 16 * (tid + i * kThreads)) = u32x4{};
+
+        // Q^T operand, resident for the whole key loop: k-step s holds
+        // q[qidx][16 s + 8 half .. +7] (zeros past N).
+        bf16x8 qop[T::kQkSteps];
+        {
+            const __bf16 *qrow = Q + head + (size_t)min(qidx, N - 1) * D + 8 * half;
+#pragma unroll
+            for (int s = 0; s < T::kQkSteps; ++s) {
+                qop[s] = *reinterpret_cast<const bf16x8 *>(qrow + 16 * s);
+                if (!q_ok)
+                    qop[s] = bf16x8{};
+            }
         }
-        f32x16 sn = {};
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+
+        f32x16 sc = {};  // scores of the block being turned into probabilities
 #pragma unroll
         for (int st = 0; st < T::kQkSteps; ++st)
-            sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*LDS_PTR(const bf16x8, kbuf + kq + koff[st]), qop[st],
-                                                         sn, 0, 0, 0);
-        pv(vbuf, vp, pb_prev);
-
-        // Row max of the next block (this lane's half of its keys, log2
-        // units), for the next step's reference.
-        float mx;
-        if constexpr (NEXT_MASKED) {
-            mx = kNegInf;
+            sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*LDS_PTR(const bf16x8, sk0 + koff[st]), qop[st], sc, 0, 0, 0);
+        f32x16 oacc[T::kOBlocks];
+#pragma unroll
+        for (int b = 0; b < T::kOBlocks; ++b)
+            oacc[b] = f32x16{};
+        // Key r of block kb (register r of the score tile) is visible to this
+        // lane's query: inside the sequence and, causal, not after the query.
+        auto visible = [&](int kb, int r) __attribute__((always_inline)) {
+            const int key = 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
+            return !(key >= N || (CAUSAL && key > qidx));
+        };
+        // Reference max m_ref of this lane's row (log2 units, scores times
+        // c_log2), the value subtracted before exp2 (m_ref, or 0 while nothing
+        // is visible) and the largest score the reference still serves.
+        float m_ref, m_sub, m_thr;
+        auto set_ref = [&](float m) __attribute__((always_inline)) {
+            m_ref = m;
+            m_sub = (m == kNegInf) ? 0.f : m;
+            m_thr = m + kRefSlack;
+        };
+        {  // block 0 sets the first reference: its exact row max
+            float mx = kNegInf;
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                mx = fmaxf(mx, visible(k + 1, r) ? sn[r] * c_log2 : kNegInf);
-        } else {  // every key visible and c_log2 > 0
-            float r0 = sn[0];
-#pragma unroll
-            for (int r = 1; r < 16; ++r)
-                r0 = fmaxf(r0, sn[r]);
-            mx = r0 * c_log2;
+                mx = fmaxf(mx, visible(0, r) ? sc[r] * c_log2 : kNegInf);
+            set_ref(wave_half_max(mx));
         }
-        const bool reref = __builtin_amdgcn_ballot_w64(mx > m_thr) != 0;  // wave-uniform
+        float l_run = 0.f;       // sum of fp32 p over this lane's half of the keys
+        float lb_run = 0.f;      // sum of the bf16-rounded p, same keys
+        bool pending = false;    // O still to be rescaled by alpha_pend (wave-uniform)
+        float alpha_pend = 1.f;
+        bf16x8 pb_prev[2] = {bf16x8{}, bf16x8{}};  // P of the previous block (none yet: zeros)
+        const bf16x2 kOnes = __builtin_bit_cast(bf16x2, 0x3f803f80u);  // bf16 {1, 1}
 
-        // Issue order for this step's scheduling region: the 16 MFMAs (8 for
-        // the next scores, 8 for P V) each followed by a share of the softmax
-        // VALU work, so the matrix cores and the VALU stay busy together; the
-        // operand reads (8 ds_read_b128 of K, 16 ds_read_b64_tr_b16 of V) run
-        // about two MFMAs ahead of their use, hiding LDS latency with a
-        // bounded number of registers in flight.
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS read
+        // O^T += V^T P^T over the 32 keys of one block (two 16-key k-steps);
+        // the block's first V row is at byte vp of V buffer vbuf.
+        auto pv = [&](const char *vbuf, int vp, const bf16x8 *pbk) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 2 * T::kQkSteps; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);  // VALU incl. transcendental
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
-            if (LOADS && i < 2 * T::kLoadsPerWave)
-                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // tile copy (VMEM)
-        }
-        // Keep this block's P and row sums inside this step: otherwise the
-        // compiler sinks the exps and adds next to their first uses (the next
-        // step's P V and the loop latch), where no MFMA is left to hide them.
-        asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(l_run), "+v"(lb_run));
+            for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+                for (int b = 0; b < T::kOBlocks; ++b) {
+                    const int vb = vp + ks * 16 * T::kRowBytes;
+                    const u32x2 lo = __builtin_bit_cast(u32x2, vread(vbuf, vb, b, 0));
+                    const u32x2 hi = __builtin_bit_cast(u32x2, vread(vbuf, vb, b, 1));
+                    const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
+                    oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va), pbk[ks], oacc[b],
+                                                                      0, 0, 0);
+                }
+            }
+        };
 
-        // The reference moved at the previous step: O now holds P V of block
-        // k-1 as well, taken against the old reference, so rescale it here.
+        // One 32-key pipeline step (block k): the softmax of block k on the VALU
+        // interleaves with the matrix-core work of the scores of block k+1 (K rows
+        // from byte kq of buffer kbuf) and P V of block k-1 (V rows from byte vp of
+        // buffer vbuf).  The first step multiplies the zeroed V buffer by P = 0;
+        // the last computes scores of a block that does not exist and discards
+        // them.  MASKED steps apply the causal / sequence-end mask.  LOADS steps
+        // also copy K tile load_t+1 into kdst and V tile load_t into vdst, spread
+        // among their MFMAs.
+        auto step = [&](int k, const char *kbuf, int kq, const char *vbuf, int vp, auto masked_tag,
+                        auto next_masked_tag, auto loads_tag, int load_t, char *kdst, char *vdst) __attribute__((always_inline)) {
+            constexpr bool MASKED = decltype(masked_tag)::value;
+            constexpr bool NEXT_MASKED = decltype(next_masked_tag)::value;
+            constexpr bool LOADS = decltype(loads_tag)::value;
+            // Keep the per-lane LDS offsets opaque inside the loop: otherwise
+            // their sums with each buffer's constant base are hoisted out of the
+            // loop as separate registers instead of riding in the ds_read
+            // immediate offset field.
+#pragma unroll
+            for (int st = 0; st < T::kQkSteps; ++st)
+                asm volatile("" : "+v"(koff[st]));
+#pragma unroll
+            for (int b = 0; b < T::kOBlocks; ++b)
+                asm volatile("" : "+v"(voff[b][0]), "+v"(voff[b][1]));
+            // Pin the softmax inside its step: without this, loop rotation moves
+            // the first step's VALU work into the previous iteration's latch, away
+            // from the MFMAs it is meant to overlap.
+            asm volatile("" : "+v"(sc));
+
+            // Register 4j+e holds key 32 k + 8 j + 4 half + e.  This block's P
+            // is taken against m_sub (the reference max, log2 units), fixed
+            // before the step, so the exps need nothing from this block's max:
+            // the previous step checked that every visible p stays <= 2^kRefSlack.
+            // l sums the fp32 p (for the LSE), lb the bf16-rounded p that P V
+            // actually multiplies (for O).
+            float p[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], c_log2, -m_sub));
+                if constexpr (MASKED)
+                    p[r] = visible(k, r) ? p[r] : 0.f;
+            }
+            float rs0 = p[0], rs1 = p[1];
+#pragma unroll
+            for (int r = 2; r < 16; r += 2) {
+                rs0 += p[r];
+                rs1 += p[r + 1];
+            }
+            // The bf16 pairs are summed from the scalar words: summing from the
+            // elements of the packed vector (w[e] in a loop) gets all four dot
+            // products fed the first element by the compiler.
+            bf16x8 pb[2];
+            float rb0 = 0.f, rb1 = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const uint32_t w0 = pack_bf16x2(p[8 * ks + 0], p[8 * ks + 1]);
+                const uint32_t w1 = pack_bf16x2(p[8 * ks + 2], p[8 * ks + 3]);
+                const uint32_t w2 = pack_bf16x2(p[8 * ks + 4], p[8 * ks + 5]);
+                const uint32_t w3 = pack_bf16x2(p[8 * ks + 6], p[8 * ks + 7]);
+                rb0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), kOnes, rb0, false);
+                rb1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), kOnes, rb1, false);
+                rb0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), kOnes, rb0, false);
+                rb1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), kOnes, rb1, false);
+                const u32x4 w = {w0, w1, w2, w3};
+                pb[ks] = __builtin_bit_cast(bf16x8, w);
+            }
+            l_run += rs0 + rs1;
+            lb_run += rb0 + rb1;
+
+            if constexpr (LOADS) {
+                load_tile(Kh, (load_t + 1) * kBc, kdst, kdma);
+                load_tile(Vh, load_t * kBc, vdst, vdma);
+            }
+            f32x16 sn = {};
+#pragma unroll
+            for (int st = 0; st < T::kQkSteps; ++st)
+                sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*LDS_PTR(const bf16x8, kbuf + kq + koff[st]), qop[st],
+                                                             sn, 0, 0, 0);
+            pv(vbuf, vp, pb_prev);
+
+            // Row max of the next block (this lane's half of its keys, log2
+            // units), for the next step's reference.
+            float mx;
+            if constexpr (NEXT_MASKED) {
+                mx = kNegInf;
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    mx = fmaxf(mx, visible(k + 1, r) ? sn[r] * c_log2 : kNegInf);
+            } else {  // every key visible and c_log2 > 0
+                float r0 = sn[0];
+#pragma unroll
+                for (int r = 1; r < 16; ++r)
+                    r0 = fmaxf(r0, sn[r]);
+                mx = r0 * c_log2;
+            }
+            const bool reref = __builtin_amdgcn_ballot_w64(mx > m_thr) != 0;  // wave-uniform
+
+            // Issue order for this step's scheduling region: the 16 MFMAs (8 for
+            // the next scores, 8 for P V) each followed by a share of the softmax
+            // VALU work, so the matrix cores and the VALU stay busy together; the
+            // operand reads (8 ds_read_b128 of K, 16 ds_read_b64_tr_b16 of V) run
+            // about two MFMAs ahead of their use, hiding LDS latency with a
+            // bounded number of registers in flight.
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS read
+#pragma unroll
+            for (int i = 0; i < 2 * T::kQkSteps; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);  // VALU incl. transcendental
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+                if (LOADS && i < 2 * T::kLoadsPerWave)
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // tile copy (VMEM)
+            }
+            // Keep this block's P and row sums inside this step: otherwise the
+            // compiler sinks the exps and adds next to their first uses (the next
+            // step's P V and the loop latch), where no MFMA is left to hide them.
+            asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(l_run), "+v"(lb_run));
+
+            // The reference moved at the previous step: O now holds P V of block
+            // k-1 as well, taken against the old reference, so rescale it here.
+            if (pending) {
+#pragma unroll
+                for (int b = 0; b < T::kOBlocks; ++b)
+                    oacc[b] *= alpha_pend;
+            }
+            // Some row of the next block has a p above 2^kRefSlack against the
+            // current reference: move the reference to the row's exact running
+            // max (both halves of the row) and rescale the sums now, O after the
+            // next P V.
+            pending = reref;
+            if (reref) {
+                const float m_new = fmaxf(m_ref, wave_half_max(mx));
+                alpha_pend = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+                l_run *= alpha_pend;
+                lb_run *= alpha_pend;
+                set_ref(m_new);
+            }
+            sc = sn;
+            pb_prev[0] = pb[0];
+            pb_prev[1] = pb[1];
+        };
+
+        // One 64-key tile t held in K buffer P = t % 2 (V tile t-1 in V buffer
+        // 1-P).  The even step makes the last reads of K tile t and V tile t-1;
+        // after the barrier the odd step refills those buffers with K tile t+2 and
+        // V tile t+1 (past the end: zeros, no memory traffic), which land before
+        // the next barrier.
+        // NEXT_MASKED: whether the block after the tile (the first of tile t+1)
+        // needs the mask.
+        auto tile = [&](int t, auto parity_tag, auto masked_tag, auto next_masked_tag) __attribute__((always_inline)) {
+            constexpr int P = decltype(parity_tag)::value;
+            constexpr int kHalf = 32 * T::kRowBytes;
+            char *kp = P ? sk1 : sk0, *kq = P ? sk0 : sk1;
+            char *vp = P ? sv1 : sv0, *vq = P ? sv0 : sv1;
+            step(2 * t, kp, kHalf, vq, kHalf, masked_tag, masked_tag, std::false_type{}, 0, kp, vq);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            step(2 * t + 1, kq, 0, vp, 0, masked_tag, next_masked_tag, std::true_type{}, t + 1, kp, vq);
+        };
+        using P0 = std::integral_constant<int, 0>;
+        using P1 = std::integral_constant<int, 1>;
+        using Unmasked = std::false_type;
+        using Masked = std::true_type;
+
+        // Tiles [0, t_free) need no mask: below the causal diagonal of every
+        // query of the workgroup and wholly inside the sequence (and a positive
+        // scale, which the unmasked row max assumes).  t_free is made even so
+        // that the loops walk (buffer 0, buffer 1) tile pairs; the last unmasked
+        // pair is peeled because the block after it needs the mask.
+        int t_free = N / kBc;
+        if (CAUSAL)
+            t_free = min(t_free, (q0 + 1) / kBc);
+        if (!(c_log2 > 0.f))
+            t_free = 0;
+        t_free = min(t_free, ntiles) & ~1;
+        int t = 0;
+        for (; t + 2 < t_free; t += 2) {
+            tile(t, P0{}, Unmasked{}, Unmasked{});
+            tile(t + 1, P1{}, Unmasked{}, Unmasked{});
+        }
+        if (t < t_free) {
+            tile(t, P0{}, Unmasked{}, Unmasked{});
+            tile(t + 1, P1{}, Unmasked{}, Masked{});
+            t += 2;
+        }
+        for (; t < ntiles; t += 2) {
+            tile(t, P0{}, Masked{}, Masked{});
+            if (t + 1 < ntiles)
+                tile(t + 1, P1{}, Masked{}, Masked{});
+        }
+        // P V of the last block: second half of V tile ntiles-1.
+        pv((ntiles - 1) & 1 ? sv1 : sv0, 32 * T::kRowBytes, pb_prev);
         if (pending) {
 #pragma unroll
             for (int b = 0; b < T::kOBlocks; ++b)
                 oacc[b] *= alpha_pend;
         }
-        // Some row of the next block has a p above 2^kRefSlack against the
-        // current reference: move the reference to the row's exact running
-        // max (both halves of the row) and rescale the sums now, O after the
-        // next P V.
-        pending = reref;
-        if (reref) {
-            const float m_new = fmaxf(m_ref, wave_half_max(mx));
-            alpha_pend = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-            l_run *= alpha_pend;
-            lb_run *= alpha_pend;
-            set_ref(m_new);
-        }
-        sc = sn;
-        pb_prev[0] = pb[0];
-        pb_prev[1] = pb[1];
-    };
+        __builtin_amdgcn_s_waitcnt(0);  // no copy may still be writing LDS when the workgroup ends
 
-    // One 64-key tile t held in K buffer P = t % 2 (V tile t-1 in V buffer
-    // 1-P).  The even step makes the last reads of K tile t and V tile t-1;
-    // after the barrier the odd step refills those buffers with K tile t+2 and
-    // V tile t+1 (past the end: zeros, no memory traffic), which land before
-    // the next barrier.
-    // NEXT_MASKED: whether the block after the tile (the first of tile t+1)
-    // needs the mask.
-    auto tile = [&](int t, auto parity_tag, auto masked_tag, auto next_masked_tag) __attribute__((always_inline)) {
-        constexpr int P = decltype(parity_tag)::value;
-        constexpr int kHalf = 32 * T::kRowBytes;
-        char *kp = P ? sk1 : sk0, *kq = P ? sk0 : sk1;
-        char *vp = P ? sv1 : sv0, *vq = P ? sv0 : sv1;
-        step(2 * t, kp, kHalf, vq, kHalf, masked_tag, masked_tag, std::false_type{}, 0, kp, vq);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        step(2 * t + 1, kq, 0, vp, 0, masked_tag, next_masked_tag, std::true_type{}, t + 1, kp, vq);
-    };
-    using P0 = std::integral_constant<int, 0>;
-    using P1 = std::integral_constant<int, 1>;
-    using Unmasked = std::false_type;
-    using Masked = std::true_type;
-
-    // Tiles [0, t_free) need no mask: below the causal diagonal of every
-    // query of the workgroup and wholly inside the sequence (and a positive
-    // scale, which the unmasked row max assumes).  t_free is made even so
-    // that the loops walk (buffer 0, buffer 1) tile pairs; the last unmasked
-    // pair is peeled because the block after it needs the mask.
-    int t_free = N / kBc;
-    if (CAUSAL)
-        t_free = min(t_free, (q0 + 1) / kBc);
-    if (!(c_log2 > 0.f))
-        t_free = 0;
-    t_free = min(t_free, ntiles) & ~1;
-    int t = 0;
-    for (; t + 2 < t_free; t += 2) {
-        tile(t, P0{}, Unmasked{}, Unmasked{});
-        tile(t + 1, P1{}, Unmasked{}, Unmasked{});
-    }
-    if (t < t_free) {
-        tile(t, P0{}, Unmasked{}, Unmasked{});
-        tile(t + 1, P1{}, Unmasked{}, Masked{});
-        t += 2;
-    }
-    for (; t < ntiles; t += 2) {
-        tile(t, P0{}, Masked{}, Masked{});
-        if (t + 1 < ntiles)
-            tile(t + 1, P1{}, Masked{}, Masked{});
-    }
-    // P V of the last block: second half of V tile ntiles-1.
-    pv((ntiles - 1) & 1 ? sv1 : sv0, 32 * T::kRowBytes, pb_prev);
-    if (pending) {
+        // Epilogue: O = O / lb (the sum of the bf16 weights that built O),
+        // LSE = ln2 * (m + log2 l) from the fp32 sum.
+        const float l_tot = wave_half_sum(l_run);
+        const float lb_tot = wave_half_sum(lb_run);
+        if (q_ok) {
+            const float inv = 1.f / lb_tot;
+            __bf16 *orow = O + head + (size_t)qidx * D;
 #pragma unroll
-        for (int b = 0; b < T::kOBlocks; ++b)
-            oacc[b] *= alpha_pend;
-    }
-    __builtin_amdgcn_s_waitcnt(0);  // no copy may still be writing LDS when the workgroup ends
-
-    // Epilogue: O = O / lb (the sum of the bf16 weights that built O),
-    // LSE = ln2 * (m + log2 l) from the fp32 sum.
-    const float l_tot = wave_half_sum(l_run);
-    const float lb_tot = wave_half_sum(lb_run);
-    if (!q_ok)
-        return;
-    const float inv = 1.f / lb_tot;
-    __bf16 *orow = O + head + (size_t)qidx * D;
+            for (int b = 0; b < T::kOBlocks; ++b) {
 #pragma unroll
-    for (int b = 0; b < T::kOBlocks; ++b) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            u32x2 w;
-            w[0] = pack_bf16x2(oacc[b][4 * j + 0] * inv, oacc[b][4 * j + 1] * inv);
-            w[1] = pack_bf16x2(oacc[b][4 * j + 2] * inv, oacc[b][4 * j + 3] * inv);
-            *reinterpret_cast<u32x2 *>(orow + 32 * b + 8 * j + 4 * half) = w;
+                for (int j = 0; j < 4; ++j) {
+                    u32x2 w;
+                    w[0] = pack_bf16x2(oacc[b][4 * j + 0] * inv, oacc[b][4 * j + 1] * inv);
+                    w[1] = pack_bf16x2(oacc[b][4 * j + 2] * inv, oacc[b][4 * j + 3] * inv);
+                    *reinterpret_cast<u32x2 *>(orow + 32 * b + 8 * j + 4 * half) = w;
+                }
+            }
+            if (LSE != nullptr && half == 0)
+                LSE[(size_t)bh * N + qidx] = (m_ref + __builtin_log2f(l_tot)) * 0.69314718055994530942f;
         }
     }
-    if (LSE != nullptr && half == 0)
-        LSE[(size_t)bh * N + qidx] = (m_ref + __builtin_log2f(l_tot)) * 0.69314718055994530942f;
 #endif
 }
 
@@ -581,7 +597,7 @@ template <int D, bool CAUSAL>
 static hipError_t launch(const AttnLaunch &a)
 {
     const int nqt = (int)((a.N + kBr - 1) / kBr);
-    const int n_wg = (int)(a.BH * nqt);
+    const int n_wg = (int)(a.BH * (CAUSAL ? (nqt + 1) / 2 : nqt));
     hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL>), dim3(n_wg), dim3(kThreads), 0, a.stream,
                        (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v, (__bf16 *)a.o, a.lse,
                        (int)a.N, n_wg, nqt, a.scale * 1.44269504088896340736f);
