@@ -12,8 +12,9 @@
 // the end.  Scores and probabilities live only in registers.
 //
 // gfx950 mapping
-//   * 4 waves of 64 lanes, 32 query rows per wave, 128 per workgroup, two
-//     workgroups per CU.
+//   * 32 query rows per 64-lane wave.  d = 128: 8 waves (256 queries) per
+//     workgroup, one workgroup per CU; d = 64: 4 waves (128 queries), two
+//     workgroups per CU.  Either way two waves share each SIMD.
 //   * Each wave computes the TRANSPOSED score tile S^T = K Q^T with
 //     v_mfma_f32_32x32x16_bf16: in the 32x32 accumulator layout a lane holds
 //     one column (one query) and 16 of the 32 rows (keys), so a query's row
@@ -81,12 +82,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T *)(p))
 
 constexpr int kWave = 64;
-constexpr int kWaves = 4;
-constexpr int kThreads = kWave * kWaves;
 constexpr int kRowsPerWave = 32;
-constexpr int kBr = kRowsPerWave * kWaves;  // query rows per workgroup
-constexpr int kBc = 64;                     // keys per K/V tile (two 32-key blocks)
-constexpr int kXcds = 8;                    // MI355X: 8 XCDs, workgroups dealt round-robin
+constexpr int kBrMin = 128;  // fewest query rows per workgroup (d = 64)
+constexpr int kBc = 64;      // keys per K/V tile (two 32-key blocks)
+constexpr int kXcds = 8;     // MI355X: 8 XCDs, workgroups dealt round-robin
 constexpr float kNegInf = -__builtin_inff();
 // A block's probabilities are taken against a reference max that may lag
 // the true running max by up to kRefSlack (log2 units): p <= 2^16.  A row
@@ -96,8 +95,18 @@ constexpr float kRefSlack = 16.f;
 // out-of-range offsets returning zero.
 constexpr int kBufferFlags = 0x00020000;
 
+// Workgroup shape per head dim.  d = 128: 8 waves (256 queries), one
+// workgroup per CU, two waves per SIMD from the same workgroup: each K/V
+// tile copied into LDS serves twice the queries, which halves the L2->LDS
+// copy traffic per flop (the copies cost shader clock under the chip's power
+// limit).  d = 64: 4 waves (128 queries), two workgroups per CU, so that the
+// smaller d = 64 problems still fill the chip.
 template <int D>
 struct Tile {
+    static constexpr int kWaves = D == 128 ? 8 : 4;
+    static constexpr int kThreads = kWave * kWaves;
+    static constexpr int kBr = kRowsPerWave * kWaves;  // query rows per workgroup
+    static constexpr int kWgPerCu = D == 128 ? 1 : 2;
     static constexpr int kRowBytes = D * 2;
     static constexpr int kChunks = D / 8;                  // 16-byte chunks per row
     static constexpr int kBytes = kBc * kRowBytes;         // one K or V tile
@@ -195,7 +204,7 @@ __device__ __forceinline__ void unit_of(int wg, int n_wg, int n_units, int &bh, 
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
+__global__ __launch_bounds__(Tile<D>::kThreads, Tile<D>::kWgPerCu) void attn_fwd_kernel(
     const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
     __bf16 *__restrict__ O, float *__restrict__ LSE, int N, int n_wg, int nqt, float c_log2)
 {
@@ -228,7 +237,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
         const int qt = CAUSAL ? (pass == 0 ? nqt - 1 - unit : unit) : unit;
         if (pass > 0)
             __syncthreads();  // every wave is done with the previous tile's LDS
-        const int q0 = qt * kBr;
+        const int q0 = qt * T::kBr;
         const size_t head = (size_t)bh * (size_t)N * D;
         // Copies go through buffer resources over this head's K and V: offsets at
         // or past N rows are out of range and read as zeros.
@@ -240,7 +249,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
         const int qidx = qw0 + n;
         const bool q_ok = qidx < N;
 
-        const int kv_end = CAUSAL ? min(N, q0 + kBr) : N;
+        const int kv_end = CAUSAL ? min(N, q0 + T::kBr) : N;
         const int ntiles = (kv_end + kBc - 1) / kBc;
 
         // ---- per-lane offsets, fixed for the whole loop ----
@@ -300,8 +309,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
         load_tile(Kh, kBc, sk1, kdma);
         load_tile(Vh, 0, sv0, vdma);
 #pragma unroll
-        for (int i = 0; i < T::kBytes / (16 * kThreads); ++i)
-            *LDS_PTR(u32x4, sv1 + 16 * (tid + i * kThreads)) = u32x4{};
+        for (int i = 0; i < T::kBytes / (16 * T::kThreads); ++i)
+            *LDS_PTR(u32x4, sv1 + 16 * (tid + i * T::kThreads)) = u32x4{};
 
         // Q^T operand, resident for the whole key loop: k-step s holds
         // q[qidx][16 s + 8 half .. +7] (zeros past N).
@@ -529,6 +538,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
             __syncthreads();
             step(2 * t + 1, kq, 0, vp, 0, masked_tag, next_masked_tag, std::true_type{}, t + 1, kp, vq);
         };
+        // A tile whose every step is dead for this wave under the causal mask:
+        // P V of its first step's block 2t-1 and everything after start past
+        // the wave's last query.  The wave still copies its share of the
+        // tiles and meets the barrier, so the other waves see no difference.
+        const int last_live = (qw0 + kRowsPerWave - 1) / 32;  // last 32-key block with a visible key
+        auto dead = [&](int t) __attribute__((always_inline)) { return CAUSAL && 2 * t - 1 > last_live; };
+        auto ghost = [&](int t, auto parity_tag) __attribute__((always_inline)) {
+            constexpr int P = decltype(parity_tag)::value;
+            char *kp = P ? sk1 : sk0;
+            char *vq = P ? sv0 : sv1;
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            load_tile(Kh, (t + 2) * kBc, kp, kdma);
+            load_tile(Vh, (t + 1) * kBc, vq, vdma);
+        };
         using P0 = std::integral_constant<int, 0>;
         using P1 = std::integral_constant<int, 1>;
         using Unmasked = std::false_type;
@@ -556,9 +580,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
             t += 2;
         }
         for (; t < ntiles; t += 2) {
-            tile(t, P0{}, Masked{}, Masked{});
-            if (t + 1 < ntiles)
-                tile(t + 1, P1{}, Masked{}, Masked{});
+            if (dead(t))
+                ghost(t, P0{});
+            else
+                tile(t, P0{}, Masked{}, Masked{});
+            if (t + 1 < ntiles) {
+                if (dead(t + 1))
+                    ghost(t + 1, P1{});
+                else
+                    tile(t + 1, P1{}, Masked{}, Masked{});
+            }
         }
         // P V of the last block: second half of V tile ntiles-1.
         pv((ntiles - 1) & 1 ? sv1 : sv0, 32 * T::kRowBytes, pb_prev);
@@ -596,9 +627,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(
 template <int D, bool CAUSAL>
 static hipError_t launch(const AttnLaunch &a)
 {
-    const int nqt = (int)((a.N + kBr - 1) / kBr);
+    using T = Tile<D>;
+    const int nqt = (int)((a.N + T::kBr - 1) / T::kBr);
     const int n_wg = (int)(a.BH * (CAUSAL ? (nqt + 1) / 2 : nqt));
-    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL>), dim3(n_wg), dim3(kThreads), 0, a.stream,
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL>), dim3(n_wg), dim3(T::kThreads), 0, a.stream,
                        (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v, (__bf16 *)a.o, a.lse,
                        (int)a.N, n_wg, nqt, a.scale * 1.44269504088896340736f);
     return hipGetLastError();
@@ -608,7 +640,8 @@ static hipError_t launch(const AttnLaunch &a)
 
 int64_t attn_workgroups(int64_t BH, int64_t N)
 {
-    return BH * ((N + attn_gfx950::kBr - 1) / attn_gfx950::kBr);
+    // An upper bound over head dims and masks: the smallest query tile.
+    return BH * ((N + attn_gfx950::kBrMin - 1) / attn_gfx950::kBrMin);
 }
 
 hipError_t attn_launch(const AttnLaunch &a)

@@ -17,7 +17,7 @@ struct AttnLaunch {
     hipStream_t stream;
 };
 
-// Workgroups one call launches for B*H heads of length N.
+// An upper bound on the workgroups one call launches for B*H heads of length N.
 int64_t attn_workgroups(int64_t BH, int64_t N);
 
 // Enqueue the kernel; returns hipGetLastError() after the launch.
