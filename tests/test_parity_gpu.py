@@ -105,6 +105,35 @@ def test_ragged_lengths(N, d, causal):
 
 
 @pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 33, 100, 1000])
+def test_memory_past_the_sequence_is_never_read(N, d, causal):
+    """K and V sit at the start of a NaN-filled allocation, so every row past
+    N of the last head is NaN.  A copy that read one (instead of the zeros
+    the range-checked loads return) would turn O into NaN through 0 * NaN."""
+    from exact_io_aware_27_amd import attn
+    B, H = 1, 2
+    q, k, v = inputs.make_qkv(B, H, N, d, seed=2000 + N + d + causal)
+    say("case: NaN past the end", (B, H, N, d), "causal" if causal else "non-causal")
+    n = B * H * N * d
+    pad = 64 * 1024 * d  # far more than one key tile past the end
+    kbig = torch.full((n + pad,), float("nan"), dtype=torch.bfloat16, device=DEV)
+    vbig = torch.full((n + pad,), float("nan"), dtype=torch.bfloat16, device=DEV)
+    kbig[:n].copy_(k.reshape(-1).to(DEV))
+    vbig[:n].copy_(v.reshape(-1).to(DEV))
+    kd, vd = kbig[:n].view(B, H, N, d), vbig[:n].view(B, H, N, d)
+    qd = q.to(DEV)
+    o = torch.empty_like(qd)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=DEV)
+    attn.attn_fwd(qd, kd, vd, o, lse, B, H, N, d, causal, 1.0 / math.sqrt(d), torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention(q, k, v, causal, 1.0 / math.sqrt(d))
+    rep = parity.compare(o, lse, o_ref, lse_ref)
+    say("  ", rep)
+    parity.assert_parity(rep, "NaN past the end N=%d d=%d" % (N, d))
+
+
+@pytest.mark.parametrize("d", [64, 128])
 def test_many_heads_and_batches(d):
     q, k, v = inputs.make_qkv(3, 5, 300, d, seed=77)
     check_full(q, k, v, True, 1.0 / math.sqrt(d), "B=3 H=5 N=300")
