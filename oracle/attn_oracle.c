@@ -22,8 +22,11 @@
  * Readings where the pages are silent (each is also listed in the design doc):
  *   - the scale is an explicit argument; every workload passes 1/sqrt(d),
  *     the value in the attention equation;
- *   - causal: key j is visible to query i iff j <= i (Nq == Nk, so there is
- *     no alignment question); masked keys take no part in max, sum or output;
+ *   - causal: key j is visible to query i iff j <= i + (Nk - Nq).  With
+ *     Nq == Nk that is j <= i; with fewer queries than keys the queries are
+ *     the LAST Nq positions of the sequence (each new token sees every key
+ *     before it, as in decoding with the keys and values of earlier tokens
+ *     kept); masked keys take no part in max, sum or output;
  *   - LSE (the saved softmax statistics, m and l, folded into one number) is
  *     the natural-log logsumexp of the scaled, masked logits: m + ln(l);
  *   - inputs are bfloat16 bit patterns; each is widened exactly to fp64.
@@ -55,8 +58,9 @@ static double widen_bf16(uint16_t bits)
 }
 
 typedef struct {
-    const uint16_t *q, *k, *v; /* [BH][N][d] bf16 bits */
-    int64_t BH, N, d;
+    const uint16_t *q;         /* [BH][Nq][d] bf16 bits */
+    const uint16_t *k, *v;     /* [BH][Nk][d] bf16 bits */
+    int64_t BH, Nq, Nk, d;
     int causal;
     double scale;
     const int64_t *rows; /* [BH][R] query-row indices, or NULL = all rows */
@@ -74,7 +78,7 @@ enum { ROWS_PER_JOB = 64 };
 
 /*
  * One query row i of one (batch, head):
- *   J    = {0..N-1}, or {0..i} when causal
+ *   J    = {0..Nk-1}, or {0..i+Nk-Nq} when causal
  *   S_j  = scale * sum_t q_it k_jt            (the S row, materialised)
  *   m    = max_j S_j
  *   e_j  = exp(S_j - m),  l = sum_j e_j,  P_j = e_j / l   (the P row)
@@ -85,11 +89,11 @@ static int one_row(const oracle_ctx *c, int64_t bh, int64_t i, double *qrow,
                    double *S, double *P, double *o_out, double *lse_out,
                    double *dev_out)
 {
-    const int64_t N = c->N, d = c->d;
-    const uint16_t *q = c->q + bh * N * d;
-    const uint16_t *k = c->k + bh * N * d;
-    const uint16_t *v = c->v + bh * N * d;
-    const int64_t nkeys = c->causal ? i + 1 : N;
+    const int64_t Nq = c->Nq, Nk = c->Nk, d = c->d;
+    const uint16_t *q = c->q + bh * Nq * d;
+    const uint16_t *k = c->k + bh * Nk * d;
+    const uint16_t *v = c->v + bh * Nk * d;
+    const int64_t nkeys = c->causal ? i + (Nk - Nq) + 1 : Nk;
 
     for (int64_t t = 0; t < d; ++t)
         qrow[t] = widen_bf16(q[i * d + t]);
@@ -136,8 +140,8 @@ static void *worker(void *arg)
     oracle_ctx *c = (oracle_ctx *)arg;
     const int64_t jobs_per_bh = (c->R + ROWS_PER_JOB - 1) / ROWS_PER_JOB;
     double *qrow = malloc((size_t)c->d * sizeof(double));
-    double *S = malloc((size_t)c->N * sizeof(double));
-    double *P = malloc((size_t)c->N * sizeof(double));
+    double *S = malloc((size_t)c->Nk * sizeof(double));
+    double *P = malloc((size_t)c->Nk * sizeof(double));
     int status = ORACLE_OK;
     if (!qrow || !S || !P)
         status = ORACLE_NO_MEMORY;
@@ -173,28 +177,30 @@ static void *worker(void *arg)
 }
 
 /*
- * oracle_attn: exact attention for the selected query rows of every
- * (batch, head).
- *   q, k, v   bf16 bit patterns, contiguous [BH][N][d]
- *   rows      [BH][R] query indices in [0, N), or NULL for R == N, all rows
+ * oracle_attn_qk: exact attention for the selected query rows of every
+ * (batch, head), Nq queries against Nk keys.
+ *   q         bf16 bit patterns, contiguous [BH][Nq][d]
+ *   k, v      bf16 bit patterns, contiguous [BH][Nk][d]
+ *   causal    requires Nq <= Nk (every query then sees at least key 0)
+ *   rows      [BH][R] query indices in [0, Nq), or NULL for R == Nq, all rows
  *   o         out: fp64 [BH][R][d];  lse: out, fp64 [BH][R]
  *   psum_dev  out (optional): fp64 [BH][R], |sum_j P_ij - 1|
  *   nthreads  worker threads (>= 1)
  * Returns ORACLE_OK, or ORACLE_BAD_ARG / ORACLE_NO_MEMORY / ORACLE_PSUM.
  */
-int oracle_attn(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                int64_t BH, int64_t N, int64_t d, int causal, double scale,
-                const int64_t *rows, int64_t R, double *o, double *lse,
-                double *psum_dev, int nthreads)
+int oracle_attn_qk(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                   int64_t BH, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                   double scale, const int64_t *rows, int64_t R, double *o,
+                   double *lse, double *psum_dev, int nthreads)
 {
-    if (!q || !k || !v || !o || !lse || BH < 0 || N < 1 || d < 1 || R < 0 ||
-        nthreads < 1 || !isfinite(scale))
+    if (!q || !k || !v || !o || !lse || BH < 0 || Nq < 1 || Nk < 1 || d < 1 ||
+        R < 0 || nthreads < 1 || !isfinite(scale) || (causal && Nq > Nk))
         return ORACLE_BAD_ARG;
-    if (!rows && R != N)
+    if (!rows && R != Nq)
         return ORACLE_BAD_ARG;
     if (rows)
         for (int64_t x = 0; x < BH * R; ++x)
-            if (rows[x] < 0 || rows[x] >= N)
+            if (rows[x] < 0 || rows[x] >= Nq)
                 return ORACLE_BAD_ARG;
     if (BH == 0 || R == 0)
         return ORACLE_OK;
@@ -204,7 +210,8 @@ int oracle_attn(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     c.k = k;
     c.v = v;
     c.BH = BH;
-    c.N = N;
+    c.Nq = Nq;
+    c.Nk = Nk;
     c.d = d;
     c.causal = causal ? 1 : 0;
     c.scale = scale;
@@ -238,4 +245,14 @@ int oracle_attn(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     free(tid);
     pthread_mutex_destroy(&c.lock);
     return c.status;
+}
+
+/* oracle_attn: the same with Nq == Nk == N (queries and keys of one sequence). */
+int oracle_attn(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                int64_t BH, int64_t N, int64_t d, int causal, double scale,
+                const int64_t *rows, int64_t R, double *o, double *lse,
+                double *psum_dev, int nthreads)
+{
+    return oracle_attn_qk(q, k, v, BH, N, N, d, causal, scale, rows, R, o, lse,
+                          psum_dev, nthreads);
 }

@@ -43,13 +43,13 @@ def build(force=True):
 
 
 def load_library(path):
-    """Open a compiled oracle library and declare oracle_attn's signature."""
+    """Open a compiled oracle library and declare oracle_attn_qk's signature."""
     lib = ctypes.CDLL(path)
-    f = lib.oracle_attn
+    f = lib.oracle_attn_qk
     f.restype = ctypes.c_int
     p = ctypes.c_void_p
     i64 = ctypes.c_int64
-    f.argtypes = [p, p, p, i64, i64, i64, ctypes.c_int, ctypes.c_double,
+    f.argtypes = [p, p, p, i64, i64, i64, i64, ctypes.c_int, ctypes.c_double,
                   p, i64, p, p, p, ctypes.c_int]
     return lib
 
@@ -84,8 +84,10 @@ def _bf16_bits(x):
 
 
 def attention(q, k, v, causal, scale, rows=None, nthreads=None, return_psum_dev=False, lib=None):
-    """Exact attention in fp64 for bf16 inputs of shape [B, H, N, d].
+    """Exact attention in fp64 for bf16 q [B, H, Nq, d] and k, v [B, H, Nk, d].
 
+    Under the causal mask query i sees key j iff j <= i + (Nk - Nq): the
+    queries are the last Nq positions of the key sequence (Nq <= Nk).
     rows: None for every query row, else an int array [B*H, R] (or [B, H, R])
     of query indices per (batch, head).
     Returns (o, lse): o float64 [B, H, R, d], lse float64 [B, H, R]
@@ -93,12 +95,14 @@ def attention(q, k, v, causal, scale, rows=None, nthreads=None, return_psum_dev=
     lib: a library from load_library() to use instead of the built one.
     """
     qb, kb, vb = _bf16_bits(q), _bf16_bits(k), _bf16_bits(v)
-    if qb.ndim != 4 or qb.shape != kb.shape or qb.shape != vb.shape:
-        raise ValueError("q, k, v must share one [B, H, N, d] shape")
-    B, H, N, d = qb.shape
+    if qb.ndim != 4 or kb.shape != vb.shape or kb.ndim != 4 or qb.shape[:2] != kb.shape[:2] \
+            or qb.shape[3] != kb.shape[3]:
+        raise ValueError("q must be [B, H, Nq, d] and k, v one [B, H, Nk, d] shape")
+    B, H, Nq, d = qb.shape
+    Nk = kb.shape[2]
     BH = B * H
     if rows is None:
-        R = N
+        R = Nq
         rows_arr = None
     else:
         rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(BH, -1))
@@ -107,11 +111,11 @@ def attention(q, k, v, causal, scale, rows=None, nthreads=None, return_psum_dev=
     lse = np.empty((BH, R), dtype=np.float64)
     dev = np.empty((BH, R), dtype=np.float64)
     lib = lib or _load()
-    st = lib.oracle_attn(qb.ctypes.data, kb.ctypes.data, vb.ctypes.data, BH, N, d,
-                         1 if causal else 0, float(scale),
-                         None if rows_arr is None else rows_arr.ctypes.data, R,
-                         o.ctypes.data, lse.ctypes.data, dev.ctypes.data,
-                         int(nthreads or default_threads()))
+    st = lib.oracle_attn_qk(qb.ctypes.data, kb.ctypes.data, vb.ctypes.data, BH, Nq, Nk, d,
+                            1 if causal else 0, float(scale),
+                            None if rows_arr is None else rows_arr.ctypes.data, R,
+                            o.ctypes.data, lse.ctypes.data, dev.ctypes.data,
+                            int(nthreads or default_threads()))
     if st != 0:
         raise RuntimeError("oracle_attn failed: %s" % ORACLE_STATUS.get(st, st))
     out = (o.reshape(B, H, R, d), lse.reshape(B, H, R))

@@ -187,3 +187,59 @@ def test_rejects_bad_rows():
     q, k, v = inputs.make_qkv(1, 1, 8, 64, seed=20)
     with pytest.raises(RuntimeError):
         oracle.attention(q, k, v, False, 0.1, rows=np.array([[8]]))
+
+
+# ---- fewer queries than keys (queries are the last Nq positions) ----
+
+def _sdpa64_mask(q, k, v, causal, scale):
+    Nq, Nk = q.shape[2], k.shape[2]
+    mask = torch.ones(Nq, Nk, dtype=torch.bool).tril(diagonal=Nk - Nq) if causal else None
+    return torch.nn.functional.scaled_dot_product_attention(
+        _wide(q), _wide(k), _wide(v), attn_mask=mask, scale=scale).numpy()
+
+
+def _lse_scipy_qk(q, k, causal, scale):
+    s = scale * np.einsum("bhid,bhjd->bhij", _wide(q).numpy(), _wide(k).numpy())
+    if causal:
+        Nq, Nk = s.shape[-2:]
+        s = np.where(np.tril(np.ones((Nq, Nk), dtype=bool), k=Nk - Nq), s, -np.inf)
+    return scipy.special.logsumexp(s, axis=-1)
+
+
+@pytest.mark.parametrize("Nq,Nk,d,causal", [
+    (1, 1, 64, True), (1, 300, 64, True), (1, 300, 128, False), (4, 129, 128, True),
+    (17, 1000, 64, True), (64, 65, 128, True), (100, 333, 64, False)])
+def test_fewer_queries_match_sdpa_with_explicit_mask(Nq, Nk, d, causal):
+    q = inputs.make_qkv(2, 2, Nq, d, seed=400 + Nq)[0]
+    _, k, v = inputs.make_qkv(2, 2, Nk, d, seed=401 + Nk)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = oracle.attention(q, k, v, causal, scale)
+    np.testing.assert_allclose(o, _sdpa64_mask(q, k, v, causal, scale), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, _lse_scipy_qk(q, k, causal, scale), rtol=0, atol=1e-12)
+
+
+def test_decode_rows_are_the_last_rows_of_the_full_causal_problem():
+    # queries at the last Nq positions see exactly what those rows of the full
+    # (Nk x Nk) causal problem see
+    Nk, Nq, d = 257, 9, 128
+    q, k, v = inputs.make_qkv(1, 3, Nk, d, seed=402)
+    o_full, lse_full = oracle.attention(q, k, v, True, 0.0883)
+    o, lse = oracle.attention(q[:, :, Nk - Nq:].contiguous(), k, v, True, 0.0883)
+    assert np.array_equal(o, o_full[:, :, Nk - Nq:])
+    assert np.array_equal(lse, lse_full[:, :, Nk - Nq:])
+
+
+def test_single_causal_query_sees_every_key():
+    q = inputs.make_qkv(1, 2, 1, 64, seed=403)[0]
+    _, k, v = inputs.make_qkv(1, 2, 500, 64, seed=404)
+    a = oracle.attention(q, k, v, True, 0.125)
+    b = oracle.attention(q, k, v, False, 0.125)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_rejects_more_queries_than_keys_under_the_causal_mask():
+    q = inputs.make_qkv(1, 1, 10, 64, seed=405)[0]
+    _, k, v = inputs.make_qkv(1, 1, 9, 64, seed=406)
+    with pytest.raises(RuntimeError):
+        oracle.attention(q, k, v, True, 0.1)
+    oracle.attention(q, k, v, False, 0.1)  # fine without the mask

@@ -25,8 +25,12 @@ MUTANTS = {
     "doubled_scale": ("S[j] = c->scale * dot;", "S[j] = 2.0 * c->scale * dot;"),
     "no_max_subtraction": ("P[j] = exp(S[j] - m);", "P[j] = exp(S[j]);"),
     "min_instead_of_max": ("if (S[j] > m)", "if (S[j] < m)"),
-    "causal_excludes_diagonal": ("c->causal ? i + 1 : N", "c->causal ? (i > 0 ? i : 1) : N"),
-    "causal_wrong_direction": ("c->causal ? i + 1 : N", "c->causal ? N - i : N"),
+    "causal_excludes_diagonal": ("c->causal ? i + (Nk - Nq) + 1 : Nk",
+                                 "c->causal ? (i + (Nk - Nq) > 0 ? i + (Nk - Nq) : 1) : Nk"),
+    "causal_wrong_direction": ("c->causal ? i + (Nk - Nq) + 1 : Nk", "c->causal ? Nk - i : Nk"),
+    "causal_top_left_aligned": ("c->causal ? i + (Nk - Nq) + 1 : Nk", "c->causal ? i + 1 : Nk"),
+    "key_head_stride_of_queries": ("const uint16_t *k = c->k + bh * Nk * d;",
+                                   "const uint16_t *k = c->k + bh * Nq * d;"),
     "lse_base_two": ("*lse_out = m + log(l);", "*lse_out = m + log2(l);"),
     "lse_drops_max": ("*lse_out = m + log(l);", "*lse_out = log(l);"),
     "value_from_keys": ("o_out[t] += p * widen_bf16(v[j * d + t]);",
@@ -34,7 +38,7 @@ MUTANTS = {
     "query_times_queries": ("dot += qrow[t] * widen_bf16(k[j * d + t]);",
                             "dot += qrow[t] * widen_bf16(q[j * d + t]);"),
     "query_row_zero_only": ("qrow[t] = widen_bf16(q[i * d + t]);", "qrow[t] = widen_bf16(q[t]);"),
-    "head_offset_lost": ("const uint16_t *v = c->v + bh * N * d;", "const uint16_t *v = c->v;"),
+    "head_offset_lost": ("const uint16_t *v = c->v + bh * Nk * d;", "const uint16_t *v = c->v;"),
 }
 
 
@@ -69,6 +73,23 @@ def _pin_failures(lib):
 
     check("sdpa_causal", lambda: sdpa(65, 64, True))
     check("sdpa_noncausal", lambda: sdpa(70, 64, False))
+
+    def sdpa_fewer_queries(Nq, Nk, d, causal):
+        # the library routine with an explicit mask: key j visible to query i
+        # iff j <= i + (Nk - Nq)
+        q = inputs.make_qkv(1, 2, Nq, d, seed=310 + Nq)[0]
+        _, k, v = inputs.make_qkv(1, 2, Nk, d, seed=311 + Nk)
+        sc = 1.0 / math.sqrt(d)
+        o, _ = oracle.attention(q, k, v, causal, sc, lib=lib, nthreads=2)
+        mask = None
+        if causal:
+            mask = torch.ones(Nq, Nk, dtype=torch.bool).tril(diagonal=Nk - Nq)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            q.double(), k.double(), v.double(), attn_mask=mask, scale=sc).numpy()
+        return np.allclose(o, ref, rtol=0, atol=1e-12)
+
+    check("sdpa_fewer_queries_causal", lambda: sdpa_fewer_queries(5, 70, 64, True))
+    check("sdpa_fewer_queries_noncausal", lambda: sdpa_fewer_queries(3, 41, 64, False))
 
     for case in golden_cases.load():
         def golden(case=case):
