@@ -20,8 +20,10 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so"
 
 ATTN_OK = 0
 STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_NULL_PTR", 2: "ATTN_BAD_SHAPE", 3: "ATTN_UNSUPPORTED_D",
-                4: "ATTN_BAD_SCALE", 5: "ATTN_MISALIGNED", 6: "ATTN_ALIAS", 7: "ATTN_HIP"}
-EXPORTS = ("attn_fwd", "attn_status_string", "attn_last_hip_error")
+                4: "ATTN_BAD_SCALE", 5: "ATTN_MISALIGNED", 6: "ATTN_ALIAS", 7: "ATTN_HIP",
+                8: "ATTN_BAD_WORKSPACE"}
+EXPORTS = ("attn_fwd", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_bytes", "attn_status_string",
+           "attn_last_hip_error")
 
 _lib = None
 
@@ -49,6 +51,11 @@ def load():
     p, i64 = ctypes.c_void_p, ctypes.c_int64
     lib.attn_fwd.restype = ctypes.c_int
     lib.attn_fwd.argtypes = [p, p, p, p, p, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float, p]
+    lib.attn_fwd_splitkv.restype = ctypes.c_int
+    lib.attn_fwd_splitkv.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float,
+                                     i64, p, i64, p]
+    lib.attn_fwd_splitkv_workspace_bytes.restype = i64
+    lib.attn_fwd_splitkv_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_status_string.argtypes = [ctypes.c_int]
     lib.attn_last_hip_error.restype = ctypes.c_int
@@ -120,4 +127,63 @@ def attention(q, k, v, causal=False, scale=None, with_lse=True, stream=None):
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, stream)
+    return o, lse
+
+
+def splitkv_workspace_bytes(B, H, Nq, d, num_splits):
+    """attn_fwd_splitkv_workspace_bytes of include/attn.h (-1: invalid arguments)."""
+    return load().attn_fwd_splitkv_workspace_bytes(int(B), int(H), int(Nq), int(d), int(num_splits))
+
+
+def attn_fwd_splitkv_status(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, num_splits,
+                            workspace, workspace_bytes, stream=None):
+    """Call attn_fwd_splitkv and return its status code (0 = ATTN_OK).
+
+    q, o: bf16 [B, H, Nq, d]; k, v: bf16 [B, H, Nk, d]; lse: fp32 [B, H, Nq]
+    or None; workspace: a device tensor (its data pointer is passed), a raw
+    pointer, or None.  Tensors are checked against the shapes; raw pointers
+    are the caller's responsibility.
+    """
+    qs, ks = (int(B), int(H), int(Nq), int(d)), (int(B), int(H), int(Nk), int(d))
+    _check(q, "q", qs, torch.bfloat16)
+    _check(o, "o", qs, torch.bfloat16)
+    _check(k, "k", ks, torch.bfloat16)
+    _check(v, "v", ks, torch.bfloat16)
+    _check(lse, "lse", qs[:3], torch.float32)
+    lib = load()
+    return lib.attn_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(Nq),
+                                int(Nk), int(d), 1 if causal else 0, float(scale), int(num_splits),
+                                _ptr(workspace), int(workspace_bytes), _stream(stream))
+
+
+def attn_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, num_splits, workspace,
+                     workspace_bytes, stream=None):
+    """attn_fwd_splitkv of include/attn.h; raises AttnError on a nonzero status."""
+    st = attn_fwd_splitkv_status(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, num_splits,
+                                 workspace, workspace_bytes, stream)
+    if st != ATTN_OK:
+        raise AttnError(st, load().attn_last_hip_error() if st == 7 else 0)
+
+
+def attention_splitkv(q, k, v, num_splits, causal=False, scale=None, with_lse=True, stream=None,
+                      workspace=None):
+    """Allocate O (and LSE, and the workspace unless given) and run
+    attn_fwd_splitkv on torch's current stream.
+
+    q: contiguous bf16 CUDA tensor [B, H, Nq, d]; k, v: [B, H, Nk, d].
+    Returns (o, lse).
+    """
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if scale is None:
+        scale = d ** -0.5
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if with_lse else None
+    nbytes = splitkv_workspace_bytes(B, H, Nq, d, num_splits)
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    attn_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, num_splits, workspace,
+                     max(nbytes, 0) if workspace is not None else 0, stream)
     return o, lse

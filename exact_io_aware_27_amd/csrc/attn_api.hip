@@ -43,34 +43,52 @@ extern "C" const char *attn_status_string(int status)
     case ATTN_MISALIGNED: return "ATTN_MISALIGNED";
     case ATTN_ALIAS: return "ATTN_ALIAS";
     case ATTN_HIP: return "ATTN_HIP";
+    case ATTN_BAD_WORKSPACE: return "ATTN_BAD_WORKSPACE";
     default: return "ATTN_UNKNOWN_STATUS";
     }
 }
 
 extern "C" int attn_last_hip_error(void) { return g_last_hip_error; }
 
-extern "C" int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
-                        int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
-                        void *stream)
+namespace {
+
+// Shared validation and launch of attn_fwd and attn_fwd_splitkv, in the
+// documented order.
+int fwd_common(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B, int64_t H,
+               int64_t Nq, int64_t Nk, int64_t d, int causal, float scale, int64_t num_splits,
+               void *workspace, int64_t workspace_bytes, void *stream)
 {
     // 1. Shapes: non-negative, byte sizes and index ranges representable.
-    int64_t BH, rows, elems, bytes, lse_bytes;
-    if (B < 0 || H < 0 || N < 0 || !mul_ok(B, H, &BH) || !mul_ok(BH, N, &rows))
+    int64_t BH, qrows, krows, qelems, kelems, qbytes, kbytes, lse_bytes;
+    if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || num_splits < 1 || !mul_ok(B, H, &BH) ||
+        !mul_ok(BH, Nq, &qrows) || !mul_ok(BH, Nk, &krows))
         return ATTN_BAD_SHAPE;
     // 2. Head dimension.
     if (d != 64 && d != 128)
         return ATTN_UNSUPPORTED_D;
-    if (!mul_ok(rows, d, &elems) || !mul_ok(elems, 2, &bytes) || !mul_ok(rows, 4, &lse_bytes))
+    if (!mul_ok(qrows, d, &qelems) || !mul_ok(qelems, 2, &qbytes) || !mul_ok(krows, d, &kelems) ||
+        !mul_ok(kelems, 2, &kbytes) || !mul_ok(qrows, 4, &lse_bytes))
         return ATTN_BAD_SHAPE;
-    if (N * d >= (int64_t(1) << 31))  // in-head offsets are 32-bit in the kernel
+    if (Nq * d >= (int64_t(1) << 31) || Nk * d >= (int64_t(1) << 31))  // in-head offsets are 32-bit
         return ATTN_BAD_SHAPE;
-    if (rows > 0 && attn_workgroups(BH, N) > INT32_MAX)
+    if (qrows > 0 && (Nk == 0 || (causal && Nq > Nk)))  // a query with no key to attend to
         return ATTN_BAD_SHAPE;
+    if (qrows > 0 && attn_workgroups(BH, Nq, Nk, num_splits) > INT32_MAX)
+        return ATTN_BAD_SHAPE;
+    const int64_t splits = qrows > 0 ? attn_splits_used(Nk, num_splits) : 1;
+    int64_t ws_need = 0;
+    if (splits > 1) {
+        int64_t t;
+        if (!mul_ok(splits, qrows, &t) || !mul_ok(t, d + 1, &t) || !mul_ok(t, 4, &ws_need))
+            return ATTN_BAD_SHAPE;
+        if (qrows * (d / 8) > INT32_MAX - 255)  // one merge thread per 8 columns of a row
+            return ATTN_BAD_SHAPE;
+    }
     // 3. Scale.
     if (!std::isfinite(scale))
         return ATTN_BAD_SCALE;
     // 4. Empty problem: nothing to read or write.
-    if (rows == 0)
+    if (qrows == 0)
         return ATTN_OK;
     // 5. Pointers.
     if (!q || !k || !v || !o)
@@ -81,11 +99,19 @@ extern "C" int attn_fwd(const void *q, const void *k, const void *v, void *o, fl
         (lse && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0))
         return ATTN_MISALIGNED;
     // 7. Outputs must not overlap inputs or each other (q, k, v may alias one another).
-    if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, bytes) || overlaps(o, bytes, v, bytes))
+    if (overlaps(o, qbytes, q, qbytes) || overlaps(o, qbytes, k, kbytes) || overlaps(o, qbytes, v, kbytes))
         return ATTN_ALIAS;
-    if (lse && (overlaps(lse, lse_bytes, q, bytes) || overlaps(lse, lse_bytes, k, bytes) ||
-                overlaps(lse, lse_bytes, v, bytes) || overlaps(lse, lse_bytes, o, bytes)))
+    if (lse && (overlaps(lse, lse_bytes, q, qbytes) || overlaps(lse, lse_bytes, k, kbytes) ||
+                overlaps(lse, lse_bytes, v, kbytes) || overlaps(lse, lse_bytes, o, qbytes)))
         return ATTN_ALIAS;
+    // 8. Workspace (split ranges only).
+    if (splits > 1) {
+        if (!workspace || mis16(workspace) || workspace_bytes < ws_need ||
+            overlaps(workspace, ws_need, q, qbytes) || overlaps(workspace, ws_need, k, kbytes) ||
+            overlaps(workspace, ws_need, v, kbytes) || overlaps(workspace, ws_need, o, qbytes) ||
+            (lse && overlaps(workspace, ws_need, lse, lse_bytes)))
+            return ATTN_BAD_WORKSPACE;
+    }
 
     AttnLaunch a;
     a.q = q;
@@ -94,10 +120,13 @@ extern "C" int attn_fwd(const void *q, const void *k, const void *v, void *o, fl
     a.o = o;
     a.lse = lse;
     a.BH = BH;
-    a.N = N;
+    a.Nq = Nq;
+    a.Nk = Nk;
     a.d = d;
     a.causal = causal != 0;
     a.scale = scale;
+    a.num_splits = num_splits;
+    a.workspace = splits > 1 ? workspace : nullptr;
     a.stream = static_cast<hipStream_t>(stream);
     const hipError_t err = attn_launch(a);
     if (err != hipSuccess) {
@@ -105,4 +134,36 @@ extern "C" int attn_fwd(const void *q, const void *k, const void *v, void *o, fl
         return ATTN_HIP;
     }
     return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                        int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+                        void *stream)
+{
+    return fwd_common(q, k, v, o, lse, B, H, N, N, d, causal, scale, 1, nullptr, 0, stream);
+}
+
+extern "C" int attn_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse,
+                                int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                                float scale, int64_t num_splits, void *workspace, int64_t workspace_bytes,
+                                void *stream)
+{
+    return fwd_common(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, num_splits, workspace,
+                      workspace_bytes, stream);
+}
+
+extern "C" int64_t attn_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t d,
+                                                    int64_t num_splits)
+{
+    int64_t BH, rows, t, bytes;
+    if (B < 0 || H < 0 || Nq < 0 || num_splits < 1 || (d != 64 && d != 128) || !mul_ok(B, H, &BH) ||
+        !mul_ok(BH, Nq, &rows))
+        return -1;
+    if (num_splits == 1)
+        return 0;
+    if (!mul_ok(num_splits, rows, &t) || !mul_ok(t, d + 1, &t) || !mul_ok(t, 4, &bytes))
+        return -1;
+    return bytes;
 }

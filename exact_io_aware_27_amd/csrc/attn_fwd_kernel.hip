@@ -76,6 +76,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -203,10 +204,24 @@ __device__ __forceinline__ void unit_of(int wg, int n_wg, int n_units, int &bh, 
     unit = lin % n_units;
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(Tile<D>::kThreads, Tile<D>::kWgPerCu) void attn_fwd_kernel(
-    const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
-    __bf16 *__restrict__ O, float *__restrict__ LSE, int N, int n_wg, int nqt, float c_log2)
+// Kernel arguments.  Q, O, LSE: [BH][Nq](×d); K, V: [BH][Nk][d].  Under the
+// causal mask query i sees key j iff j <= i + (Nk - Nq) (the queries are the
+// last Nq positions of the sequence).  The key range [0, Nk) is cut into
+// n_splits ranges of split_keys keys (a multiple of two 64-key tiles); with
+// SPLIT each workgroup writes its range's normalised fp32 O and its LSE to
+// Opart [n_splits][BH][Nq][d] and LSEpart [n_splits][BH][Nq] for the merge
+// kernel, else bf16 O and fp32 LSE (LSE may be null) directly.
+struct KArgs {
+    const __bf16 *Q, *K, *V;
+    __bf16 *O;
+    float *LSE;
+    float *Opart, *LSEpart;
+    int BH, Nq, Nk, n_wg, nqt, n_splits, split_keys;
+    float c_log2;
+};
+
+template <int D, bool CAUSAL, bool SPLIT>
+__global__ __launch_bounds__(Tile<D>::kThreads, Tile<D>::kWgPerCu) void attn_fwd_kernel(const KArgs a)
 {
     // The body is device code only (gfx950 buffer resources and LDS builtins);
     // the host pass needs just the declaration to emit the launch stub.
@@ -226,31 +241,64 @@ __global__ __launch_bounds__(Tile<D>::kThreads, Tile<D>::kWgPerCu) void attn_fwd
     const int n = lane & 31;     // this lane's query column in the 32x32 tiles
     const int half = lane >> 5;  // which half of the 32 keys / 16 k-values
 
+    const int Nq = a.Nq, Nk = a.Nk, nqt = a.nqt;
+    const float c_log2 = a.c_log2;
+    const int delta = Nk - Nq;  // causal offset: query i sees keys <= i + delta
+
     // Causal: unit j of a head is the pair of query tiles (nqt-1-j, j), the
     // heavy one first, so that every workgroup does nearly the same work (the
     // middle tile of an odd count is alone); non-causal: one tile per unit.
+    // Work items are ordered (head, split, unit), so that all the work on one
+    // head's keys stays on one XCD.
     const int n_units = CAUSAL ? (nqt + 1) / 2 : nqt;
-    int bh, unit;
-    unit_of(blockIdx.x, n_wg, n_units, bh, unit);
+    int bh, rem;
+    unit_of(blockIdx.x, a.n_wg, n_units * a.n_splits, bh, rem);
+    const int split = rem / n_units, unit = rem % n_units;
+    const int kv_lo = split * a.split_keys;
+    const int kv_hi = min(Nk, kv_lo + a.split_keys);
     const int npass = (CAUSAL && nqt - 1 - unit != unit) ? 2 : 1;
     for (int pass = 0; pass < npass; ++pass) {
         const int qt = CAUSAL ? (pass == 0 ? nqt - 1 - unit : unit) : unit;
         if (pass > 0)
             __syncthreads();  // every wave is done with the previous tile's LDS
         const int q0 = qt * T::kBr;
-        const size_t head = (size_t)bh * (size_t)N * D;
-        // Copies go through buffer resources over this head's K and V: offsets at
-        // or past N rows are out of range and read as zeros.
-        const int head_bytes = N * T::kRowBytes;
-        const __bf16 *Kh = K + head;
-        const __bf16 *Vh = V + head;
+        const size_t qhead = (size_t)bh * (size_t)Nq * D;
+        const size_t kvhead = (size_t)bh * (size_t)Nk * D;
+        const __bf16 *Kh = a.K + kvhead;
+        const __bf16 *Vh = a.V + kvhead;
 
         const int qw0 = q0 + wave * kRowsPerWave;  // first query of this wave
         const int qidx = qw0 + n;
-        const bool q_ok = qidx < N;
+        const bool q_ok = qidx < Nq;
 
-        const int kv_end = CAUSAL ? min(N, q0 + T::kBr) : N;
-        const int ntiles = (kv_end + kBc - 1) / kBc;
+        // This tile's keys in this split: [kv_lo, kv_end), in 64-key tiles
+        // [t_lo, t_end); t_lo is even (split_keys is a multiple of 128).
+        const int kv_end = CAUSAL ? min(kv_hi, q0 + T::kBr + delta) : kv_hi;
+        const int t_lo = kv_lo / kBc;
+        const int t_end = (kv_end + kBc - 1) / kBc;
+        // Copies go through buffer resources over this head's keys [0, kv_end):
+        // rows at or past kv_end (invisible to every query of the tile) are out
+        // of range and read as zeros with no memory access, so the prefetches
+        // past the end of the range cost nothing.
+        // (N d < 2^31 keeps byte counts below 2^32: unsigned arithmetic.)
+        const uint32_t head_bytes = (uint32_t)kv_end * (uint32_t)T::kRowBytes;
+
+        // Result of rows that see no key of this range: LSE = -inf, O = 0.
+        if (t_end <= t_lo) {
+            if constexpr (SPLIT) {
+                if (q_ok) {
+                    float *op = a.Opart + (((size_t)split * a.BH + bh) * Nq + qidx) * D;
+#pragma unroll
+                    for (int b = 0; b < T::kOBlocks; ++b)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            *reinterpret_cast<f32x4 *>(op + 32 * b + 8 * j + 4 * half) = f32x4{};
+                    if (half == 0)
+                        a.LSEpart[((size_t)split * a.BH + bh) * Nq + qidx] = kNegInf;
+                }
+            }
+            continue;
+        }
 
         // ---- per-lane offsets, fixed for the whole loop ----
         // DMA: slice i of this wave is LDS bytes [1024 s, 1024 s + 1024) of a tile
@@ -291,32 +339,32 @@ __global__ __launch_bounds__(Tile<D>::kThreads, Tile<D>::kWgPerCu) void attn_fwd
 
         // One K or V tile (64 keys from kv0) into an LDS buffer: this wave's
         // kLoadsPerWave 1 KB slices, each one buffer_load_dwordx4 ... lds.  Rows
-        // past N, and whole tiles past the end, read as zeros (no memory access),
+        // past kv_end, and whole tiles past it, read as zeros (no memory access),
         // so the copy needs no branch.
         auto load_tile = [&](const __bf16 *src, int kv0, char *buf, const uint32_t *dma) __attribute__((always_inline)) {
             const __amdgpu_buffer_rsrc_t rsrc =
-                __builtin_amdgcn_make_buffer_rsrc((void *)src, (short)0, head_bytes, kBufferFlags);
+                __builtin_amdgcn_make_buffer_rsrc((void *)src, (short)0, (int)head_bytes, kBufferFlags);
 #pragma unroll
             for (int i = 0; i < T::kLoadsPerWave; ++i)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     rsrc, LDS_PTR(void, buf + (wave_u * T::kLoadsPerWave + i) * 1024), 16, dma[i],
-                    kv0 * T::kRowBytes, 0, 0);
+                    (int)((uint32_t)kv0 * (uint32_t)T::kRowBytes), 0, 0);
         };
 
-        // Prologue: K tiles 0 and 1 and V tile 0 in flight while Q is read; V
-        // buffer 1 is zeroed for the first step's (empty) P V.
-        load_tile(Kh, 0, sk0, kdma);
-        load_tile(Kh, kBc, sk1, kdma);
-        load_tile(Vh, 0, sv0, vdma);
+        // Prologue: K tiles t_lo and t_lo+1 and V tile t_lo in flight while Q is
+        // read; V buffer 1 is zeroed for the first step's (empty) P V.
+        load_tile(Kh, kv_lo, sk0, kdma);
+        load_tile(Kh, kv_lo + kBc, sk1, kdma);
+        load_tile(Vh, kv_lo, sv0, vdma);
 #pragma unroll
         for (int i = 0; i < T::kBytes / (16 * T::kThreads); ++i)
             *LDS_PTR(u32x4, sv1 + 16 * (tid + i * T::kThreads)) = u32x4{};
 
         // Q^T operand, resident for the whole key loop: k-step s holds
-        // q[qidx][16 s + 8 half .. +7] (zeros past N).
+        // q[qidx][16 s + 8 half .. +7] (zeros past Nq).
         bf16x8 qop[T::kQkSteps];
         {
-            const __bf16 *qrow = Q + head + (size_t)min(qidx, N - 1) * D + 8 * half;
+            const __bf16 *qrow = a.Q + qhead + (size_t)min(qidx, Nq - 1) * D + 8 * half;
 #pragma unroll
             for (int s = 0; s < T::kQkSteps; ++s) {
                 qop[s] = *reinterpret_cast<const bf16x8 *>(qrow + 16 * s);
@@ -336,10 +384,10 @@ __global__ __launch_bounds__(Tile<D>::kThreads, Tile<D>::kWgPerCu) void attn_fwd
         for (int b = 0; b < T::kOBlocks; ++b)
             oacc[b] = f32x16{};
         // Key r of block kb (register r of the score tile) is visible to this
-        // lane's query: inside the sequence and, causal, not after the query.
+        // lane's query: inside this key range and, causal, not after the query.
         auto visible = [&](int kb, int r) __attribute__((always_inline)) {
             const int key = 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-            return !(key >= N || (CAUSAL && key > qidx));
+            return !(key >= kv_hi || (CAUSAL && key > qidx + delta));
         };
         // Reference max m_ref of this lane's row (log2 units, scores times
         // c_log2), the value subtracted before exp2 (m_ref, or 0 while nothing
@@ -350,11 +398,16 @@ __global__ __launch_bounds__(Tile<D>::kThreads, Tile<D>::kWgPerCu) void attn_fwd
             m_sub = (m == kNegInf) ? 0.f : m;
             m_thr = m + kRefSlack;
         };
-        {  // block 0 sets the first reference: its exact row max
+        {  // the range's first block sets the first reference: its exact row max
+            // (keys counted from kv_lo: key kv_lo + kr is visible iff kr < kv_hi - kv_lo
+            // and, causal, kr <= qidx + delta - kv_lo)
+            const int lim_hi = kv_hi - kv_lo, lim_q = CAUSAL ? qidx + delta - kv_lo : 0x7fffffff;
             float mx = kNegInf;
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                mx = fmaxf(mx, visible(0, r) ? sc[r] * c_log2 : kNegInf);
+            for (int r = 0; r < 16; ++r) {
+                const int kr = 8 * (r >> 2) + 4 * half + (r & 3);
+                mx = fmaxf(mx, (kr < lim_hi && kr <= lim_q) ? sc[r] * c_log2 : kNegInf);
+            }
             set_ref(wave_half_max(mx));
         }
         float l_run = 0.f;       // sum of fp32 p over this lane's half of the keys
@@ -542,7 +595,7 @@ __global__ __launch_bounds__(Tile<D>::kThreads, Tile<D>::kWgPerCu) void attn_fwd
         // P V of its first step's block 2t-1 and everything after start past
         // the wave's last query.  The wave still copies its share of the
         // tiles and meets the barrier, so the other waves see no difference.
-        const int last_live = (qw0 + kRowsPerWave - 1) / 32;  // last 32-key block with a visible key
+        const int last_live = (qw0 + kRowsPerWave - 1 + delta) / 32;  // last 32-key block with a visible key
         auto dead = [&](int t) __attribute__((always_inline)) { return CAUSAL && 2 * t - 1 > last_live; };
         auto ghost = [&](int t, auto parity_tag) __attribute__((always_inline)) {
             constexpr int P = decltype(parity_tag)::value;
@@ -558,96 +611,214 @@ __global__ __launch_bounds__(Tile<D>::kThreads, Tile<D>::kWgPerCu) void attn_fwd
         using Unmasked = std::false_type;
         using Masked = std::true_type;
 
-        // Tiles [0, t_free) need no mask: below the causal diagonal of every
-        // query of the workgroup and wholly inside the sequence (and a positive
-        // scale, which the unmasked row max assumes).  t_free is made even so
-        // that the loops walk (buffer 0, buffer 1) tile pairs; the last unmasked
-        // pair is peeled because the block after it needs the mask.
-        int t_free = N / kBc;
+        // Tiles [t_lo, t_free) need no mask: inside the key range and below the
+        // causal diagonal of every query of the workgroup (and a positive scale,
+        // which the unmasked row max assumes).  t_free - t_lo is made even so
+        // that the loops walk (buffer 0, buffer 1) tile pairs (t_lo is even);
+        // the last unmasked pair is peeled because the block after it needs the
+        // mask.
+        int t_free = kv_hi / kBc;
         if (CAUSAL)
-            t_free = min(t_free, (q0 + 1) / kBc);
+            t_free = min(t_free, (q0 + delta + 1) / kBc);
         if (!(c_log2 > 0.f))
-            t_free = 0;
-        t_free = min(t_free, ntiles) & ~1;
-        int t = 0;
-        for (; t + 2 < t_free; t += 2) {
-            tile(t, P0{}, Unmasked{}, Unmasked{});
-            tile(t + 1, P1{}, Unmasked{}, Unmasked{});
-        }
-        if (t < t_free) {
-            tile(t, P0{}, Unmasked{}, Unmasked{});
-            tile(t + 1, P1{}, Unmasked{}, Masked{});
-            t += 2;
-        }
-        for (; t < ntiles; t += 2) {
-            if (dead(t))
+            t_free = t_lo;
+        t_free = max(t_lo, min(t_free, t_end));
+        t_free = t_lo + ((t_free - t_lo) & ~1);
+        int t = t_lo;
+        if (qw0 >= Nq) {
+            // No query of this wave exists: copy its share of every tile and
+            // meet every barrier, nothing else.
+            for (; t < t_end; t += 2) {
                 ghost(t, P0{});
-            else
-                tile(t, P0{}, Masked{}, Masked{});
-            if (t + 1 < ntiles) {
-                if (dead(t + 1))
+                if (t + 1 < t_end)
                     ghost(t + 1, P1{});
-                else
-                    tile(t + 1, P1{}, Masked{}, Masked{});
             }
-        }
-        // P V of the last block: second half of V tile ntiles-1.
-        pv((ntiles - 1) & 1 ? sv1 : sv0, 32 * T::kRowBytes, pb_prev);
-        if (pending) {
+        } else {
+            for (; t + 2 < t_free; t += 2) {
+                tile(t, P0{}, Unmasked{}, Unmasked{});
+                tile(t + 1, P1{}, Unmasked{}, Unmasked{});
+            }
+            if (t < t_free) {
+                tile(t, P0{}, Unmasked{}, Unmasked{});
+                tile(t + 1, P1{}, Unmasked{}, Masked{});
+                t += 2;
+            }
+            for (; t < t_end; t += 2) {
+                if (dead(t))
+                    ghost(t, P0{});
+                else
+                    tile(t, P0{}, Masked{}, Masked{});
+                if (t + 1 < t_end) {
+                    if (dead(t + 1))
+                        ghost(t + 1, P1{});
+                    else
+                        tile(t + 1, P1{}, Masked{}, Masked{});
+                }
+            }
+            // P V of the last block: second half of V tile t_end-1.
+            pv((t_end - 1) & 1 ? sv1 : sv0, 32 * T::kRowBytes, pb_prev);
+            if (pending) {
 #pragma unroll
-            for (int b = 0; b < T::kOBlocks; ++b)
-                oacc[b] *= alpha_pend;
+                for (int b = 0; b < T::kOBlocks; ++b)
+                    oacc[b] *= alpha_pend;
+            }
         }
         __builtin_amdgcn_s_waitcnt(0);  // no copy may still be writing LDS when the workgroup ends
 
         // Epilogue: O = O / lb (the sum of the bf16 weights that built O),
-        // LSE = ln2 * (m + log2 l) from the fp32 sum.
+        // LSE = ln2 * (m + log2 l) from the fp32 sum.  In a key range where a
+        // row sees no key (split mode only) l = lb = 0: LSE = -inf, O = 0.
         const float l_tot = wave_half_sum(l_run);
         const float lb_tot = wave_half_sum(lb_run);
         if (q_ok) {
-            const float inv = 1.f / lb_tot;
-            __bf16 *orow = O + head + (size_t)qidx * D;
+            const float inv = lb_tot > 0.f ? 1.f / lb_tot : 0.f;
+            const float lse = (m_ref + __builtin_log2f(l_tot)) * 0.69314718055994530942f;
+            if constexpr (SPLIT) {
+                float *op = a.Opart + (((size_t)split * a.BH + bh) * Nq + qidx) * D;
 #pragma unroll
-            for (int b = 0; b < T::kOBlocks; ++b) {
+                for (int b = 0; b < T::kOBlocks; ++b)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    u32x2 w;
-                    w[0] = pack_bf16x2(oacc[b][4 * j + 0] * inv, oacc[b][4 * j + 1] * inv);
-                    w[1] = pack_bf16x2(oacc[b][4 * j + 2] * inv, oacc[b][4 * j + 3] * inv);
-                    *reinterpret_cast<u32x2 *>(orow + 32 * b + 8 * j + 4 * half) = w;
+                    for (int j = 0; j < 4; ++j)
+                        *reinterpret_cast<f32x4 *>(op + 32 * b + 8 * j + 4 * half) =
+                            f32x4{oacc[b][4 * j + 0] * inv, oacc[b][4 * j + 1] * inv, oacc[b][4 * j + 2] * inv,
+                                  oacc[b][4 * j + 3] * inv};
+                if (half == 0)
+                    a.LSEpart[((size_t)split * a.BH + bh) * Nq + qidx] = l_tot > 0.f ? lse : kNegInf;
+            } else {
+                __bf16 *orow = a.O + qhead + (size_t)qidx * D;
+#pragma unroll
+                for (int b = 0; b < T::kOBlocks; ++b) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        u32x2 w;
+                        w[0] = pack_bf16x2(oacc[b][4 * j + 0] * inv, oacc[b][4 * j + 1] * inv);
+                        w[1] = pack_bf16x2(oacc[b][4 * j + 2] * inv, oacc[b][4 * j + 3] * inv);
+                        *reinterpret_cast<u32x2 *>(orow + 32 * b + 8 * j + 4 * half) = w;
+                    }
                 }
+                if (a.LSE != nullptr && half == 0)
+                    a.LSE[(size_t)bh * Nq + qidx] = lse;
             }
-            if (LSE != nullptr && half == 0)
-                LSE[(size_t)bh * N + qidx] = (m_ref + __builtin_log2f(l_tot)) * 0.69314718055994530942f;
         }
     }
 #endif
 }
 
-template <int D, bool CAUSAL>
-static hipError_t launch(const AttnLaunch &a)
+// Merge of the split ranges (the two-block merge equation of "FlashAttention
+// evolution", letsgetai.github.io, core-mechanism section, applied to S
+// blocks): LSE = log sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s.  One
+// thread per 8 head-dim columns of one query row; memory-bound (it reads
+// S (4 d + 4) bytes and writes 2 d + 4 bytes per row), so it is laid out for
+// 16-byte coalesced loads and stores and nothing else.
+template <int D>
+__global__ __launch_bounds__(256) void attn_merge_kernel(const float *__restrict__ Opart,
+                                                        const float *__restrict__ LSEpart,
+                                                        __bf16 *__restrict__ O, float *__restrict__ LSE,
+                                                        int rows, int S)
+{
+    constexpr int kChunks = D / 8;
+    const int gid = blockIdx.x * blockDim.x + threadIdx.x;
+    const int row = gid / kChunks, c = gid % kChunks;
+    if (row >= rows)
+        return;
+    constexpr float kLog2e = 1.44269504088896340736f;
+    float m = kNegInf;
+    for (int s = 0; s < S; ++s)
+        m = fmaxf(m, LSEpart[(size_t)s * rows + row]);
+    f32x4 acc0 = {}, acc1 = {};
+    float wsum = 0.f;
+    if (m != kNegInf) {
+        for (int s = 0; s < S; ++s) {
+            const float ls = LSEpart[(size_t)s * rows + row];
+            const float w = __builtin_amdgcn_exp2f((ls - m) * kLog2e);  // 0 for an empty range
+            const float *src = Opart + ((size_t)s * rows + row) * D + 8 * c;
+            acc0 += w * *reinterpret_cast<const f32x4 *>(src);
+            acc1 += w * *reinterpret_cast<const f32x4 *>(src + 4);
+            wsum += w;
+        }
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    u32x4 out;
+    out[0] = pack_bf16x2(acc0[0] * inv, acc0[1] * inv);
+    out[1] = pack_bf16x2(acc0[2] * inv, acc0[3] * inv);
+    out[2] = pack_bf16x2(acc1[0] * inv, acc1[1] * inv);
+    out[3] = pack_bf16x2(acc1[2] * inv, acc1[3] * inv);
+    *reinterpret_cast<u32x4 *>(O + (size_t)row * D + 8 * c) = out;
+    if (LSE != nullptr && c == 0)
+        LSE[row] = wsum > 0.f ? m + __builtin_logf(wsum) : kNegInf;
+}
+
+template <int D, bool CAUSAL, bool SPLIT>
+static hipError_t launch(const AttnLaunch &a, int splits, int split_keys)
 {
     using T = Tile<D>;
-    const int nqt = (int)((a.N + T::kBr - 1) / T::kBr);
-    const int n_wg = (int)(a.BH * (CAUSAL ? (nqt + 1) / 2 : nqt));
-    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL>), dim3(n_wg), dim3(T::kThreads), 0, a.stream,
-                       (const __bf16 *)a.q, (const __bf16 *)a.k, (const __bf16 *)a.v, (__bf16 *)a.o, a.lse,
-                       (int)a.N, n_wg, nqt, a.scale * 1.44269504088896340736f);
+    KArgs k;
+    k.Q = (const __bf16 *)a.q;
+    k.K = (const __bf16 *)a.k;
+    k.V = (const __bf16 *)a.v;
+    k.O = (__bf16 *)a.o;
+    k.LSE = a.lse;
+    k.Opart = SPLIT ? (float *)a.workspace : nullptr;
+    k.LSEpart = SPLIT ? (float *)a.workspace + (size_t)splits * a.BH * a.Nq * D : nullptr;
+    k.BH = (int)a.BH;
+    k.Nq = (int)a.Nq;
+    k.Nk = (int)a.Nk;
+    k.nqt = (int)((a.Nq + T::kBr - 1) / T::kBr);
+    k.n_splits = splits;
+    k.split_keys = split_keys;
+    k.n_wg = (int)(a.BH * (CAUSAL ? (k.nqt + 1) / 2 : k.nqt) * splits);
+    k.c_log2 = a.scale * 1.44269504088896340736f;
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, SPLIT>), dim3(k.n_wg), dim3(T::kThreads), 0, a.stream, k);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || !SPLIT)
+        return err;
+    const int rows = (int)(a.BH * a.Nq);
+    const int threads = rows * (D / 8);
+    hipLaunchKernelGGL((attn_merge_kernel<D>), dim3((threads + 255) / 256), dim3(256), 0, a.stream,
+                       (const float *)k.Opart, (const float *)k.LSEpart, (__bf16 *)a.o, a.lse, rows, splits);
     return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch_mode(const AttnLaunch &a)
+{
+    const int64_t splits = attn_splits_used(a.Nk, a.num_splits);
+    if (splits <= 1)
+        return launch<D, CAUSAL, false>(a, 1, (int)attn_split_keys(a.Nk, 1));
+    return launch<D, CAUSAL, true>(a, (int)splits, (int)attn_split_keys(a.Nk, a.num_splits));
 }
 
 }  // namespace attn_gfx950
 
-int64_t attn_workgroups(int64_t BH, int64_t N)
+int64_t attn_split_keys(int64_t Nk, int64_t num_splits)
+{
+    // ceil(Nk / num_splits) rounded up to two 64-key tiles, so every range
+    // starts on an even tile
+    const int64_t per = (Nk + num_splits - 1) / num_splits;
+    return ((per + 127) / 128) * 128;
+}
+
+int64_t attn_splits_used(int64_t Nk, int64_t num_splits)
+{
+    const int64_t keys = attn_split_keys(Nk, num_splits);
+    return keys > 0 ? (Nk + keys - 1) / keys : 1;
+}
+
+int64_t attn_splitkv_workspace_bytes(int64_t BH, int64_t Nq, int64_t d, int64_t num_splits)
+{
+    return num_splits * BH * Nq * (d + 1) * 4;
+}
+
+int64_t attn_workgroups(int64_t BH, int64_t Nq, int64_t Nk, int64_t num_splits)
 {
     // An upper bound over head dims and masks: the smallest query tile.
-    return BH * ((N + attn_gfx950::kBrMin - 1) / attn_gfx950::kBrMin);
+    return BH * ((Nq + attn_gfx950::kBrMin - 1) / attn_gfx950::kBrMin) * attn_splits_used(Nk, num_splits);
 }
 
 hipError_t attn_launch(const AttnLaunch &a)
 {
     using namespace attn_gfx950;
     if (a.d == 128)
-        return a.causal ? launch<128, true>(a) : launch<128, false>(a);
-    return a.causal ? launch<64, true>(a) : launch<64, false>(a);
+        return a.causal ? launch_mode<128, true>(a) : launch_mode<128, false>(a);
+    return a.causal ? launch_mode<64, true>(a) : launch_mode<64, false>(a);
 }

@@ -5,20 +5,31 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-// Arguments of one validated attn_fwd call.  Sizes are already checked:
-// d is 64 or 128, N * d < 2^31, and the workgroup count fits in an int.
+// Arguments of one validated call.  Sizes are already checked: d is 64 or
+// 128, Nq * d and Nk * d are below 2^31, Nq <= Nk under the causal mask, and
+// the workgroup count fits in an int.
 struct AttnLaunch {
-    const void *q, *k, *v;
-    void *o;
-    float *lse;  // may be null
-    int64_t BH, N, d;
+    const void *q, *k, *v;  // q: [BH][Nq][d]; k, v: [BH][Nk][d]
+    void *o;                // [BH][Nq][d]
+    float *lse;             // [BH][Nq] or null
+    int64_t BH, Nq, Nk, d;
     bool causal;
     float scale;
+    int64_t num_splits;  // key ranges; 1 = one pass straight into o and lse
+    void *workspace;     // num_splits > 1: attn_splitkv_workspace_bytes() bytes
     hipStream_t stream;
 };
 
-// An upper bound on the workgroups one call launches for B*H heads of length N.
-int64_t attn_workgroups(int64_t BH, int64_t N);
+// Keys per split range (a multiple of 128) and the number of non-empty
+// ranges that num_splits asks for.
+int64_t attn_split_keys(int64_t Nk, int64_t num_splits);
+int64_t attn_splits_used(int64_t Nk, int64_t num_splits);
 
-// Enqueue the kernel; returns hipGetLastError() after the launch.
+// Bytes of workspace a split call needs: fp32 O and LSE of every range.
+int64_t attn_splitkv_workspace_bytes(int64_t BH, int64_t Nq, int64_t d, int64_t num_splits);
+
+// An upper bound on the workgroups one call launches.
+int64_t attn_workgroups(int64_t BH, int64_t Nq, int64_t Nk, int64_t num_splits);
+
+// Enqueue the kernel(s); returns hipGetLastError() after the launches.
 hipError_t attn_launch(const AttnLaunch &a);

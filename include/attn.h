@@ -24,8 +24,11 @@
  * saved softmax statistics m + ln(l) that a recomputing backward pass needs
  * ("FlashAttention evolution", recomputation paragraph).
  *
- * Causal mask: key j is visible to query i iff j <= i.  Masked logits take no
- * part in the max, the sum or the output.
+ * Causal mask: key j is visible to query i iff j <= i + (Nk - Nq); with as
+ * many queries as keys (attn_fwd) that is j <= i.  Fewer queries than keys
+ * (attn_fwd_splitkv) are the last Nq positions of the sequence, as when
+ * decoding with the keys and values of earlier tokens kept.  Masked logits
+ * take no part in the max, the sum or the output.
  */
 #ifndef EXACT_IO_AWARE_ATTN_H
 #define EXACT_IO_AWARE_ATTN_H
@@ -42,17 +45,21 @@
 extern "C" {
 #endif
 
-/* Status codes returned by attn_fwd(). */
+/* Status codes returned by attn_fwd() and attn_fwd_splitkv(). */
 enum attn_status {
     ATTN_OK = 0,
     ATTN_NULL_PTR = 1,      /* q, k, v or o is NULL (and the problem is not empty) */
-    ATTN_BAD_SHAPE = 2,     /* B, H or N negative; N * d >= 2^31; a byte size or the
-                               workgroup count overflows */
+    ATTN_BAD_SHAPE = 2,     /* B, H, N (Nq, Nk) negative; N * d >= 2^31; a byte size or
+                               the workgroup count overflows; split-KV only: Nk == 0
+                               with queries, causal Nq > Nk, num_splits < 1 */
     ATTN_UNSUPPORTED_D = 3, /* d is neither 64 nor 128 */
     ATTN_BAD_SCALE = 4,     /* scale is NaN or infinite */
     ATTN_MISALIGNED = 5,    /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
     ATTN_ALIAS = 6,         /* o or lse overlaps q, k or v, or o overlaps lse */
-    ATTN_HIP = 7            /* the kernel launch failed; see attn_last_hip_error() */
+    ATTN_HIP = 7,           /* the kernel launch failed; see attn_last_hip_error() */
+    ATTN_BAD_WORKSPACE = 8  /* attn_fwd_splitkv: workspace NULL, not 16-byte aligned,
+                               smaller than attn_fwd_splitkv_workspace_bytes(), or
+                               overlapping q, k, v, o or lse */
 };
 
 /*
@@ -84,6 +91,47 @@ enum attn_status {
 ATTN_API int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
              int64_t B, int64_t H, int64_t N, int64_t d, int causal,
              float scale, void *stream);
+
+/*
+ * attn_fwd_splitkv -- the same result with the keys cut into ranges that
+ * separate workgroups process in parallel, then merged: FlashDecoding's
+ * parallelism over the key sequence ("FlashAttention" concept page,
+ * compassingai.com, section 5, evolution timeline) with the two-block merge
+ * equation of "FlashAttention evolution" (letsgetai.github.io, core-mechanism
+ * section) applied to the ranges: LSE = log sum_s exp(LSE_s) and
+ * O = sum_s exp(LSE_s - LSE) O_s.  It keeps the chip busy when B * H * Nq is
+ * small next to Nk (few heads, or decoding with Nq = 1).
+ *
+ * q, o     bf16, contiguous [B][H][Nq][d];  lse: fp32 [B][H][Nq] or NULL.
+ * k, v     bf16, contiguous [B][H][Nk][d].
+ * Nq, Nk   queries and keys per head, Nk >= 1; under the causal mask
+ *          Nq <= Nk (the queries are the last Nq positions).  Nq == 0, B == 0
+ *          or H == 0 is an immediate no-op.
+ * num_splits  requested key ranges, >= 1.  A range holds
+ *          ceil(Nk / num_splits) keys rounded up to a multiple of 128, so
+ *          fewer ranges may be used.  When one range results (num_splits
+ *          == 1, or Nk <= 128), one pass writes o and lse directly and the
+ *          workspace is not touched (and may be NULL).
+ * workspace, workspace_bytes  device scratch for the per-range fp32 O and
+ *          LSE, at least attn_fwd_splitkv_workspace_bytes(B, H, Nq, d,
+ *          num_splits) bytes, 16-byte aligned, owned by the caller.  Its
+ *          contents on entry are ignored and on return are undefined; two
+ *          calls in flight must not share one workspace.
+ * Other arguments, ownership and asynchrony as attn_fwd (two kernels are
+ * enqueued when more than one range is used).  Errors are checked in the
+ * order of attn_fwd, with num_splits < 1 and causal Nq > Nk as BAD_SHAPE,
+ * then BAD_WORKSPACE after ALIAS.
+ */
+ATTN_API int attn_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse,
+                     int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                     int causal, float scale, int64_t num_splits,
+                     void *workspace, int64_t workspace_bytes, void *stream);
+
+/* Bytes of workspace attn_fwd_splitkv needs (0 for num_splits == 1);
+ * -1 if the arguments are invalid (negative, d not 64/128, num_splits < 1,
+ * or the size overflows). */
+ATTN_API int64_t attn_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t d,
+                                          int64_t num_splits);
 
 /* Static, human-readable name of a status code ("ATTN_OK", ...). */
 ATTN_API const char *attn_status_string(int status);

@@ -29,7 +29,8 @@ def _declared():
 
 
 def test_header_declares_the_abi():
-    assert set(_declared()) == {"attn_fwd", "attn_status_string", "attn_last_hip_error"}
+    assert set(_declared()) == {"attn_fwd", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_bytes",
+                                "attn_status_string", "attn_last_hip_error"}
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -43,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_status_strings(lib):
     names = ["ATTN_OK", "ATTN_NULL_PTR", "ATTN_BAD_SHAPE", "ATTN_UNSUPPORTED_D",
-             "ATTN_BAD_SCALE", "ATTN_MISALIGNED", "ATTN_ALIAS", "ATTN_HIP"]
+             "ATTN_BAD_SCALE", "ATTN_MISALIGNED", "ATTN_ALIAS", "ATTN_HIP", "ATTN_BAD_WORKSPACE"]
     for code, name in enumerate(names):
         assert lib.attn_status_string(code).decode() == name
     assert lib.attn_status_string(99).decode() == "ATTN_UNKNOWN_STATUS"
@@ -82,6 +83,46 @@ def test_lse_null_is_allowed_past_validation_order(lib):
 def test_q_k_v_may_alias_each_other(lib):
     # Shared inputs are legal; the only error left is the misaligned output.
     assert _call(lib, k=Q, v=Q, o=O + 4) == 5
+
+
+W = 0x60000000  # fake workspace address
+
+
+def _split(lib, q=Q, k=K, v=V, o=O, lse=L, B=2, H=3, Nq=7, Nk=1000, d=128, causal=1, scale=0.1,
+           S=4, ws=W, wsb=None):
+    if wsb is None:
+        wsb = lib.attn_fwd_splitkv_workspace_bytes(B, H, Nq, d, S)
+    return lib.attn_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, S, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Nq=-1), 2), (dict(Nk=-1), 2), (dict(S=0), 2), (dict(S=-3), 2),
+    (dict(Nk=0), 2),                                # queries with no key
+    (dict(Nq=1001, Nk=1000), 2),                    # causal: a query would see no key
+    (dict(Nk=1 << 24), 2),                          # Nk * d = 2^31
+    (dict(d=96), 3), (dict(scale=float("nan")), 4),
+    (dict(Nq=0, q=None, o=None, ws=None), 0), (dict(B=0, ws=None), 0),
+    (dict(q=None), 1), (dict(k=Q + 8), 5), (dict(o=K + 64), 6), (dict(lse=Q), 6),
+    (dict(ws=None), 8), (dict(ws=W + 8), 8), (dict(wsb=100), 8),
+    (dict(ws=Q), 8), (dict(ws=L - 64), 8), (dict(ws=O), 8),
+])
+def test_splitkv_argument_errors_before_any_hip_call(lib, kw, status):
+    assert _split(lib, **kw) == status
+
+
+def test_splitkv_causal_needs_no_more_queries_than_keys_only_under_the_mask(lib):
+    # non-causal Nq > Nk passes the shape checks and stops at the misaligned output
+    assert _split(lib, Nq=1001, Nk=1000, causal=0, o=O + 4) == 5
+
+
+def test_splitkv_workspace_bytes(lib):
+    f = lib.attn_fwd_splitkv_workspace_bytes
+    assert f(2, 3, 7, 128, 4) == 4 * 2 * 3 * 7 * 129 * 4
+    assert f(1, 1, 1, 64, 16) == 16 * 65 * 4
+    assert f(2, 3, 7, 128, 1) == 0
+    for bad in [(-1, 3, 7, 128, 4), (2, 3, -7, 128, 4), (2, 3, 7, 96, 4), (2, 3, 7, 128, 0),
+                (1 << 40, 1 << 20, 1 << 10, 128, 64)]:
+        assert f(*bad) == -1
 
 
 def test_binding_rejects_mismatched_tensors():
