@@ -125,6 +125,92 @@ def cpu_baseline(w, q, k, v, o_gpu, lse_gpu, rows_per_head):
         "max_abs_dLSE": float(dl.max())}
 
 
+def bench_splitkv(args):
+    """One JSON line for a split-KV workload (attn_fwd_splitkv): decode is
+    bounded by HBM (K and V read once), one long head by the MFMAs.  The same
+    problem with one key range is timed beside it."""
+    import torch
+    import numpy as np
+
+    import oracle
+    from exact_io_aware_27_amd import attn, inputs
+
+    attn.load()
+    w = {x.name: x for x in inputs.SPLITKV_WORKLOADS}[args.splitkv]
+    splits = args.splits or w.splits
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = inputs.make_q_kv(w.B, w.H, w.Nq, w.Nk, w.d, w.seed)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    od = torch.empty_like(qd)
+    lsed = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+    nbytes = attn.splitkv_workspace_bytes(w.B, w.H, w.Nq, w.d, splits)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(S):
+        nb = attn.splitkv_workspace_bytes(w.B, w.H, w.Nq, w.d, S)
+
+        def step():
+            attn.attn_fwd_splitkv(qd, kd, vd, od, lsed, w.B, w.H, w.Nq, w.Nk, w.d, w.causal, w.scale, S,
+                                  ws, nb, stream)
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms1 = timed(1)
+    ms = timed(splits)  # last: od and lsed hold the split result
+    hbm_bound = w.Nq * 4 < w.Nk // 64  # a handful of queries per key: memory-bound
+    if hbm_bound:
+        metric, unit = "split-KV decode K/V read GB/s, 1 GPU", "GB/s"
+        value = w.kv_bytes / (ms * 1e-3) / 1e9
+        one_range = w.kv_bytes / (ms1 * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(value / HBM_PEAK_GBPS, 4), "traffic": None}
+    else:
+        metric, unit = "split-KV attn fwd TFLOP/s, 1 GPU", "TFLOP/s"
+        value = w.flops / (ms * 1e-3) / 1e12
+        one_range = w.flops / (ms1 * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(value, 2), "peak": round(PEAK_BF16_TFLOPS, 1),
+                "unit": "TFLOP/s", "frac": round(value / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    out = {"metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": w.describe(), "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+                      "causal": w.causal, "splits": splits, "seed": w.seed},
+           "roofline": roof, "one_range": {"value": round(one_range, 2), "unit": unit, "ms_per_step": round(ms1, 5)}}
+    if args.cpu_rows > 0:
+        R = min(w.Nq, w.rows_checked or w.Nq, args.cpu_rows)
+        rows = torch.stack([inputs.row_subset(w.Nq, R, w.seed, bh, (0, w.Nq - 1)) for bh in range(w.B * w.H)])
+        threads = oracle.oracle.default_threads()
+        t0 = time.perf_counter()
+        o_ref, lse_ref = oracle.attention(q, k, v, w.causal, w.scale, rows=rows, nthreads=threads)
+        dt = time.perf_counter() - t0
+        off = w.Nk - w.Nq
+        keys = (rows + off + 1).double() if w.causal else torch.full(rows.shape, float(w.Nk), dtype=torch.float64)
+        flops = float(keys.sum()) * 4 * w.d
+        og = torch.gather(od.reshape(w.B * w.H, w.Nq, w.d), 1,
+                          rows.to(dev)[:, :, None].expand(-1, -1, w.d)).double().cpu().numpy()
+        lg = torch.gather(lsed.reshape(w.B * w.H, w.Nq), 1, rows.to(dev)).double().cpu().numpy()
+        out["cpu_baseline"] = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+                               "sample": "%d query rows per head (%d rows), every visible key; %.3g counted flops "
+                                         "in %.1f s" % (R, rows.numel(), flops, dt)}
+        out["parity_sampled_rows"] = {"rows": int(rows.numel()),
+                                      "max_abs_dO": float(np.abs(og - o_ref.reshape(og.shape)).max()),
+                                      "max_abs_dLSE": float(np.abs(lg - lse_ref.reshape(lg.shape)).max())}
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -134,6 +220,9 @@ def main():
                     help="name of a workload in exact_io_aware_27_amd.inputs.WORKLOADS")
     ap.add_argument("--cpu-rows", type=int, default=1024,
                     help="query rows per head in the oracle's CPU-baseline sample (0: skip)")
+    ap.add_argument("--splitkv", default=None,
+                    help="measure attn_fwd_splitkv on a workload of exact_io_aware_27_amd.inputs.SPLITKV_WORKLOADS")
+    ap.add_argument("--splits", type=int, default=0, help="key ranges for --splitkv (0: the workload's)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (HBM counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -150,6 +239,9 @@ def main():
         print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
               "(the path has no multi-GPU mode)" % args.gpus, file=sys.stderr)
         return 2
+
+    if args.splitkv:
+        return bench_splitkv(args)
 
     import torch
 

@@ -55,6 +55,67 @@ WORKLOADS = [
 HEADLINE = WORKLOADS[2]
 
 
+@dataclass(frozen=True)
+class SplitWorkload:
+    """A split-KV workload: Nq queries against Nk keys, cut into `splits` key
+    ranges (queries at the last Nq positions under the causal mask)."""
+    name: str
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    d: int
+    causal: bool
+    splits: int
+    seed: int
+    rows_checked: int  # query rows per (batch, head) the oracle checks; 0 = all
+
+    @property
+    def scale(self):
+        return 1.0 / (self.d ** 0.5)
+
+    @property
+    def visible_pairs(self):
+        """Visible (query, key) pairs per head."""
+        if not self.causal:
+            return self.Nq * self.Nk
+        off = self.Nk - self.Nq  # query i sees keys 0 .. i + off
+        return self.Nq * (off + 1) + self.Nq * (self.Nq - 1) // 2
+
+    @property
+    def flops(self):
+        return 4.0 * self.B * self.H * self.visible_pairs * self.d
+
+    @property
+    def kv_bytes(self):
+        """K and V read once (bf16)."""
+        return 2 * 2 * self.B * self.H * self.Nk * self.d
+
+    def describe(self):
+        return "%s B=%d H=%d Nq=%d Nk=%d d=%d %s splits=%d" % (
+            self.name, self.B, self.H, self.Nq, self.Nk, self.d,
+            "causal" if self.causal else "non-causal", self.splits)
+
+
+# Split-KV workloads: decoding (one new query per head against 64K cached
+# keys; memory-bound) and one long head (too few query tiles to fill the
+# chip without splitting the keys).
+SPLITKV_WORKLOADS = [
+    SplitWorkload("decode_64k", 4, 32, 1, 65536, 128, True, 4, 11, 0),
+    SplitWorkload("one_head_16k", 1, 1, 16384, 16384, 128, False, 4, 12, 256),
+]
+
+
+def make_q_kv(B, H, Nq, Nk, d, seed, sigma_qk=1.0, sigma_v=1.0):
+    """Q [B, H, Nq, d], then K and V [B, H, Nk, d], CPU bfloat16, one generator."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    q = (torch.randn((B, H, Nq, d), generator=g, dtype=torch.float32) * sigma_qk).to(torch.bfloat16)
+    k = (torch.randn((B, H, Nk, d), generator=g, dtype=torch.float32) * sigma_qk).to(torch.bfloat16)
+    v = (torch.randn((B, H, Nk, d), generator=g, dtype=torch.float32) * sigma_v).to(torch.bfloat16)
+    return q, k, v
+
+
 def make_qkv(B, H, N, d, seed, sigma_qk=1.0, sigma_v=1.0):
     """Q, K, V as CPU bfloat16 tensors [B, H, N, d], drawn in that order."""
     g = torch.Generator(device="cpu")

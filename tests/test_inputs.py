@@ -50,3 +50,27 @@ def test_workload_table():
     assert len(names) == 5 and inputs.HEADLINE.N == 8192 and inputs.HEADLINE.causal
     assert inputs.HEADLINE.flops == 4 * 2 * 32 * 8192 ** 2 * 128 / 2
     assert inputs.WORKLOADS[3].sigma_qk == 4.0 and not inputs.WORKLOADS[3].causal
+
+
+def test_make_q_kv_matches_make_qkv_when_lengths_agree():
+    a = inputs.make_q_kv(2, 3, 17, 17, 64, seed=9)
+    b = inputs.make_qkv(2, 3, 17, 64, seed=9)
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+def test_make_q_kv_shapes_and_determinism():
+    q, k, v = inputs.make_q_kv(1, 2, 3, 50, 128, seed=10)
+    assert q.shape == (1, 2, 3, 128) and k.shape == v.shape == (1, 2, 50, 128)
+    q2, k2, v2 = inputs.make_q_kv(1, 2, 3, 50, 128, seed=10)
+    assert torch.equal(q, q2) and torch.equal(k, k2) and torch.equal(v, v2)
+
+
+def test_split_workload_visible_pairs_by_brute_force():
+    for w in [inputs.SplitWorkload("t", 1, 1, 5, 9, 64, True, 2, 1, 0),
+              inputs.SplitWorkload("t", 1, 1, 5, 9, 64, False, 2, 1, 0),
+              inputs.SplitWorkload("t", 1, 1, 7, 7, 64, True, 2, 1, 0)]:
+        off = w.Nk - w.Nq
+        n = sum(1 for i in range(w.Nq) for j in range(w.Nk) if (not w.causal) or j <= i + off)
+        assert w.visible_pairs == n
+    d = {w.name: w for w in inputs.SPLITKV_WORKLOADS}["decode_64k"]
+    assert d.kv_bytes == 2 * 2 * 4 * 32 * 65536 * 128 and d.visible_pairs == 65536

@@ -1,0 +1,64 @@
+"""The compiled step schedule of the headline kernel instance (CPU only).
+
+Each 32-key step of attn_fwd_kernel<128, causal, one pass> is meant to
+interleave its 16 MFMAs with the softmax VALU work and the LDS operand reads
+(sched_group_barrier in the source).  Small, equivalent source changes have
+made the compiler fall back to source order instead: the whole softmax
+first, then each MFMA behind its own LDS read, about 11% slower on MI355X.
+This test compiles the kernel to gfx950 assembly with the same flags as the
+build and checks, for every loop of that instance whose body holds a full
+step, that the first MFMA is issued within a handful of instructions of the
+loop head.
+"""
+
+import os
+import re
+import subprocess
+
+import pytest
+
+from exact_io_aware_27_amd import build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KERNEL = os.path.join(ROOT, "exact_io_aware_27_amd", "csrc", "attn_fwd_kernel.hip")
+INSTANCE = "_ZN11attn_gfx95015attn_fwd_kernelILi128ELb1ELb0EEEvNS_5KArgsE"
+SKIP = re.compile(r"^\s*(;|$)")
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    hipcc = build.HIPCC
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    out = str(tmp_path_factory.mktemp("asm") / "kernel.s")
+    flags = [f for f in build.FLAGS if f not in ("-shared", "-fPIC") and not f.startswith("-Wl,")]
+    subprocess.check_call([hipcc] + flags + ["--cuda-device-only", "-S", "-o", out, KERNEL])
+    with open(out) as f:
+        return f.read().splitlines()
+
+
+def _instance(lines, name):
+    start = next(i for i, l in enumerate(lines) if l.startswith(name + ":"))
+    end = next(i for i in range(start, len(lines)) if "s_endpgm" in lines[i])
+    return lines[start:end + 1]
+
+
+def test_headline_steps_interleave_mfma_with_softmax(asm):
+    body = _instance(asm, INSTANCE)
+    heads = [i for i, l in enumerate(body) if "Loop Header: Depth=" in l]
+    checked = 0
+    for h in heads:
+        instrs = []
+        for l in body[h:h + 600]:
+            if "s_barrier" in l:
+                break
+            if SKIP.match(l) or l.lstrip().startswith(".") or "ASMSTART" in l or "ASMEND" in l:
+                continue
+            instrs.append(l.split()[0])
+        if sum(1 for x in instrs if x.startswith("v_mfma")) < 8:
+            continue  # not a compute step (the copy-only loop of idle waves)
+        first = next(i for i, x in enumerate(instrs) if x.startswith("v_mfma"))
+        assert first <= 12, "step at loop head %d issues %d instructions before its first MFMA: %s" % (
+            h, first, " ".join(instrs[:first + 1]))
+        checked += 1
+    assert checked >= 2, "expected the unmasked and the masked step loops"
