@@ -1,14 +1,14 @@
-"""The compiled step schedule of the headline kernel instance (CPU only).
+"""The compiled step schedule of every kernel instance (CPU only).
 
-Each 32-key step of attn_fwd_kernel<128, causal, one pass> is meant to
+Each 32-key step of attn_fwd_kernel is meant to
 interleave its 16 MFMAs with the softmax VALU work and the LDS operand reads
 (sched_group_barrier in the source).  Small, equivalent source changes have
 made the compiler fall back to source order instead: the whole softmax
 first, then each MFMA behind its own LDS read, about 11% slower on MI355X.
 This test compiles the kernel to gfx950 assembly with the same flags as the
-build and checks, for every loop of that instance whose body holds a full
-step, that the first MFMA is issued within a handful of instructions of the
-loop head.
+build and checks, for every instance (head dim, mask, one pass or key
+ranges) and every loop whose body holds a full step, that the first MFMA is
+issued within a handful of instructions of the loop head.
 """
 
 import os
@@ -21,7 +21,8 @@ from exact_io_aware_27_amd import build
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL = os.path.join(ROOT, "exact_io_aware_27_amd", "csrc", "attn_fwd_kernel.hip")
-INSTANCE = "_ZN11attn_gfx95015attn_fwd_kernelILi128ELb1ELb0EEEvNS_5KArgsE"
+INSTANCES = ["_ZN11attn_gfx95015attn_fwd_kernelILi%dELb%dELb%dEEEvNS_5KArgsE" % (d, c, s)
+             for d in (128, 64) for c in (1, 0) for s in (0, 1)]
 SKIP = re.compile(r"^\s*(;|$)")
 
 
@@ -43,8 +44,9 @@ def _instance(lines, name):
     return lines[start:end + 1]
 
 
-def test_headline_steps_interleave_mfma_with_softmax(asm):
-    body = _instance(asm, INSTANCE)
+@pytest.mark.parametrize("instance", INSTANCES)
+def test_steps_interleave_mfma_with_softmax(asm, instance):
+    body = _instance(asm, instance)
     heads = [i for i, l in enumerate(body) if "Loop Header: Depth=" in l]
     checked = 0
     for h in heads:
