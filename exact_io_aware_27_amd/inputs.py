@@ -116,6 +116,14 @@ def make_q_kv(B, H, Nq, Nk, d, seed, sigma_qk=1.0, sigma_v=1.0):
     return q, k, v
 
 
+def make_grad_out(B, H, Nq, d, seed, sigma=1.0):
+    """Upstream gradient dO [B, H, Nq, d] for the backward pass, CPU bfloat16,
+    standard normal times sigma from its own generator."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    return (torch.randn((B, H, Nq, d), generator=g, dtype=torch.float32) * sigma).to(torch.bfloat16)
+
+
 def make_qkv(B, H, N, d, seed, sigma_qk=1.0, sigma_v=1.0):
     """Q, K, V as CPU bfloat16 tensors [B, H, N, d], drawn in that order."""
     g = torch.Generator(device="cpu")

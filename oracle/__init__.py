@@ -7,10 +7,13 @@ library never imports it; the two share no code.
 
 - ``attention``: the plain definition, O = softmax(scale*QK^T)V and
   LSE = m + ln(l), in C (``attn_oracle.c``), fp64, threaded over row blocks.
+- ``attention_bwd``: the gradients dQ, dK, dV of that definition for an
+  upstream gradient dO, in C (``attn_bwd_oracle.c``), fp64, one thread per
+  head.
 - ``online``: the pages' tiled recurrence (running max m and running sum l)
   and the two-block merge identity, in NumPy fp64, used to pin the reading
   of the recurrence against the definition.
 """
 
-from .oracle import attention, build, library_path  # noqa: F401
+from .oracle import attention, attention_bwd, build, library_path  # noqa: F401
 from .online import merge_partials, online_attention  # noqa: F401

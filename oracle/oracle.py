@@ -1,10 +1,12 @@
-"""ctypes front end of the fp64 C oracle (``attn_oracle.c``).
+"""ctypes front end of the fp64 C oracles (``attn_oracle.c``, ``attn_bwd_oracle.c``).
 
-TEST INFRASTRUCTURE ONLY (see the package docstring).  Parity of the C code
+TEST INFRASTRUCTURE ONLY (see the package docstring).  Parity of the forward
 is pinned in tests/test_oracle.py: closed forms, PyTorch's CPU
 ``scaled_dot_product_attention`` in float64, and the two-block merge identity
 of "FlashAttention evolution" (letsgetai.github.io), section on the core
-mechanism, merge equation.
+mechanism, merge equation.  Parity of the gradients is pinned in
+tests/test_bwd_oracle.py: PyTorch autograd in float64, central finite
+differences and closed forms.
 """
 
 import ctypes
@@ -16,7 +18,10 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "attn_oracle.c")
 _LIB = os.path.join(_HERE, "libattn_oracle.so")
+_BWD_SRC = os.path.join(_HERE, "attn_bwd_oracle.c")
+_BWD_LIB = os.path.join(_HERE, "libattn_bwd_oracle.so")
 _lib = None
+_bwd_lib = None
 
 ORACLE_STATUS = {0: "OK", 1: "BAD_ARG", 2: "NO_MEMORY", 3: "PSUM"}
 
@@ -25,21 +30,27 @@ def library_path():
     return _LIB
 
 
-def build(force=True):
-    """Compile attn_oracle.c with gcc into oracle/libattn_oracle.so.
-
-    Plain -O2, no -ffast-math and no -march, so fp64 arithmetic keeps its
-    IEEE meaning and the library runs on any x86-64 host.
-    """
-    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
-        return _LIB
-    tmp = _LIB + ".tmp%d" % os.getpid()
+def _compile(src, lib, force):
+    if not force and os.path.exists(lib) and os.path.getmtime(lib) >= os.path.getmtime(src):
+        return lib
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
            "-fno-fast-math", "-ffp-contract=off", "-Wall", "-Wextra",
-           "-o", tmp, _SRC, "-lm"]
+           "-o", tmp, src, "-lm"]
     subprocess.check_call(cmd)
-    os.replace(tmp, _LIB)
-    return _LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(force=True):
+    """Compile the C oracles with gcc into oracle/libattn_oracle.so and
+    oracle/libattn_bwd_oracle.so.
+
+    Plain -O2, no -ffast-math and no -march, so fp64 arithmetic keeps its
+    IEEE meaning and the libraries run on any x86-64 host.
+    """
+    _compile(_BWD_SRC, _BWD_LIB, force)
+    return _compile(_SRC, _LIB, force)
 
 
 def load_library(path):
@@ -57,9 +68,29 @@ def load_library(path):
 def _load():
     global _lib
     if _lib is None:
-        build(force=False)
+        _compile(_SRC, _LIB, force=False)
         _lib = load_library(_LIB)
     return _lib
+
+
+def load_bwd_library(path):
+    """Open a compiled backward oracle and declare oracle_attn_bwd's signature."""
+    lib = ctypes.CDLL(path)
+    f = lib.oracle_attn_bwd
+    f.restype = ctypes.c_int
+    p = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    f.argtypes = [p, p, p, p, i64, i64, i64, i64, ctypes.c_int, ctypes.c_double,
+                  p, p, p, p, ctypes.c_int]
+    return lib
+
+
+def _load_bwd():
+    global _bwd_lib
+    if _bwd_lib is None:
+        _compile(_BWD_SRC, _BWD_LIB, force=False)
+        _bwd_lib = load_bwd_library(_BWD_LIB)
+    return _bwd_lib
 
 
 def default_threads():
@@ -122,3 +153,34 @@ def attention(q, k, v, causal, scale, rows=None, nthreads=None, return_psum_dev=
     if return_psum_dev:
         out = out + (dev.reshape(B, H, R),)
     return out
+
+
+def attention_bwd(q, k, v, do, causal, scale, nthreads=None, lib=None):
+    """Gradients of exact attention in fp64 for bf16 q, do [B, H, Nq, d] and
+    k, v [B, H, Nk, d] (causal: Nq <= Nk, query i sees key j iff
+    j <= i + Nk - Nq).
+
+    Returns (dq, dk, dv, dsum): float64 [B, H, Nq, d], [B, H, Nk, d] twice,
+    and D = rowsum(dO * O) as float64 [B, H, Nq].
+    lib: a library from load_bwd_library() to use instead of the built one.
+    """
+    qb, kb, vb, gb = _bf16_bits(q), _bf16_bits(k), _bf16_bits(v), _bf16_bits(do)
+    if qb.ndim != 4 or kb.ndim != 4 or kb.shape != vb.shape or gb.shape != qb.shape \
+            or qb.shape[:2] != kb.shape[:2] or qb.shape[3] != kb.shape[3]:
+        raise ValueError("q, do must be [B, H, Nq, d] and k, v one [B, H, Nk, d] shape")
+    B, H, Nq, d = qb.shape
+    Nk = kb.shape[2]
+    BH = B * H
+    dq = np.empty((BH, Nq, d), dtype=np.float64)
+    dk = np.empty((BH, Nk, d), dtype=np.float64)
+    dv = np.empty((BH, Nk, d), dtype=np.float64)
+    dsum = np.empty((BH, Nq), dtype=np.float64)
+    lib = lib or _load_bwd()
+    st = lib.oracle_attn_bwd(qb.ctypes.data, kb.ctypes.data, vb.ctypes.data, gb.ctypes.data,
+                             BH, Nq, Nk, d, 1 if causal else 0, float(scale),
+                             dq.ctypes.data, dk.ctypes.data, dv.ctypes.data, dsum.ctypes.data,
+                             int(nthreads or default_threads()))
+    if st != 0:
+        raise RuntimeError("oracle_attn_bwd failed: %s" % ORACLE_STATUS.get(st, st))
+    return (dq.reshape(B, H, Nq, d), dk.reshape(B, H, Nk, d), dv.reshape(B, H, Nk, d),
+            dsum.reshape(B, H, Nq))

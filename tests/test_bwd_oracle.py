@@ -1,0 +1,242 @@
+"""Pins of the fp64 backward oracle (``oracle.attention_bwd``) to things
+other than itself.
+
+The pages recompute S and P in the backward pass from the saved softmax
+statistics but do not write the gradients out ("FlashAttention evolution",
+letsgetai.github.io, recomputation paragraph); what the backward pass must
+produce is the derivative of the forward definition.  Each pin below is
+chosen so a plausible slip in attn_bwd_oracle.c fails at least one, and the
+mutant test at the end proves it for a list of such slips:
+  dropped D term / wrong sign       -> autograd, key-sum of dK, finite differences
+  dQ or dK without the scale        -> autograd, finite differences, scale 0
+  transposed operand (k for q, ...)  -> autograd
+  causal off by one / top-left      -> autograd with an explicit mask, row 0
+  D not equal to rowsum(dO * O)     -> the forward oracle's O
+"""
+
+import math
+import os
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import oracle as oracle_impl
+from exact_io_aware_27_amd import inputs
+
+
+def _case(B, H, Nq, Nk, d, seed):
+    q, k, v = inputs.make_q_kv(B, H, Nq, Nk, d, seed)
+    g = inputs.make_grad_out(B, H, Nq, d, seed + 1)
+    return q, k, v, g
+
+
+def _autograd64(q, k, v, g, causal, scale):
+    """PyTorch float64 autograd through SDPA on the CPU, causal as an explicit
+    bottom-right mask (key j visible to query i iff j <= i + Nk - Nq)."""
+    Nq, Nk = q.shape[2], k.shape[2]
+    Q, K, V = (t.double().requires_grad_() for t in (q, k, v))
+    mask = torch.ones(Nq, Nk, dtype=torch.bool).tril(diagonal=Nk - Nq) if causal else None
+    o = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=mask, scale=scale)
+    o.backward(g.double())
+    return Q.grad.numpy(), K.grad.numpy(), V.grad.numpy(), o.detach().numpy()
+
+
+def _pins(lib):
+    """Run the pin suite against one compiled backward oracle; return failing pin names."""
+    fails = []
+
+    def check(name, fn):
+        try:
+            with np.errstate(all="ignore"):
+                ok = fn()
+        except Exception:
+            ok = False
+        if not ok:
+            fails.append(name)
+
+    def autograd(B, H, Nq, Nk, d, causal, scale, seed):
+        q, k, v, g = _case(B, H, Nq, Nk, d, seed)
+        dq, dk, dv, dsum = oracle.attention_bwd(q, k, v, g, causal, scale, lib=lib, nthreads=2)
+        rq, rk, rv, o = _autograd64(q, k, v, g, causal, scale)
+        return (np.allclose(dq, rq, rtol=0, atol=1e-12) and np.allclose(dk, rk, rtol=0, atol=1e-12)
+                and np.allclose(dv, rv, rtol=0, atol=1e-12)
+                and np.allclose(dsum, (o * g.double().numpy()).sum(-1), rtol=0, atol=1e-12))
+
+    check("autograd_causal", lambda: autograd(1, 2, 45, 45, 32, True, 0.2, 500))
+    check("autograd_noncausal", lambda: autograd(2, 1, 33, 33, 64, False, 0.125, 501))
+    check("autograd_fewer_queries_causal", lambda: autograd(1, 2, 9, 40, 32, True, 0.25, 502))
+    check("autograd_fewer_queries_noncausal", lambda: autograd(1, 1, 5, 23, 16, False, 0.3, 503))
+
+    def key_sum_of_dk_is_zero():
+        # every row of dS sums to zero (sum_j P_ij (dP_ij - D_i) = D_i - D_i),
+        # so sum_j dK_j = scale * sum_i q_i sum_j dS_ij = 0 for any mask
+        q, k, v, g = _case(1, 2, 50, 50, 32, 504)
+        for causal in (False, True):
+            _, dk, _, _ = oracle.attention_bwd(q, k, v, g, causal, 0.3, lib=lib, nthreads=2)
+            if np.abs(dk.sum(axis=2)).max() > 1e-12:
+                return False
+        return True
+    check("key_sum_of_dk_is_zero", key_sum_of_dk_is_zero)
+
+    def key_sum_of_dv_is_query_sum_of_do():
+        # every row of P sums to one, so sum_j dV_j = sum_i dO_i
+        q, k, v, g = _case(1, 1, 30, 30, 16, 505)
+        for causal in (False, True):
+            _, _, dv, _ = oracle.attention_bwd(q, k, v, g, causal, 0.4, lib=lib, nthreads=1)
+            if not np.allclose(dv.sum(axis=2), g.double().numpy().sum(axis=2), rtol=0, atol=1e-12):
+                return False
+        return True
+    check("key_sum_of_dv", key_sum_of_dv_is_query_sum_of_do)
+
+    def scale_zero():
+        # P is uniform over the visible keys and neither logit gradient
+        # survives the factor scale: dQ = dK = 0, dV_j = sum_{i sees j} dO_i / n_i
+        Nq = Nk = 12
+        q, k, v, g = _case(1, 1, Nq, Nk, 16, 506)
+        dq, dk, dv, _ = oracle.attention_bwd(q, k, v, g, True, 0.0, lib=lib, nthreads=1)
+        gg = g.double().numpy()[0, 0]
+        want = np.zeros((Nk, 16))
+        for i in range(Nq):
+            want[:i + 1] += gg[i] / (i + 1)
+        return (np.abs(dq).max() == 0 and np.abs(dk).max() == 0
+                and np.allclose(dv[0, 0], want, rtol=0, atol=1e-13))
+    check("scale_zero", scale_zero)
+
+    def causal_row_zero():
+        # query 0 sees key 0 alone: P_00 = 1, so dQ_0 = 0 and D_0 = dO_0 . v_0
+        q, k, v, g = _case(1, 1, 20, 20, 32, 507)
+        dq, _, _, dsum = oracle.attention_bwd(q, k, v, g, True, 0.5, lib=lib, nthreads=1)
+        d0 = float(g.double()[0, 0, 0] @ v.double()[0, 0, 0])
+        return np.abs(dq[0, 0, 0]).max() == 0 and abs(dsum[0, 0, 0] - d0) < 1e-13
+    check("causal_row_zero", causal_row_zero)
+
+    def finite_differences():
+        # d/dt of sum(dO * O(x + t e)) at t = 0, central differences in fp64
+        # on the forward definition, for random directions e in Q, K and V
+        Nq, Nk, d, scale = 6, 9, 8, 0.7
+        q, k, v, g = _case(1, 1, Nq, Nk, d, 508)
+        for causal in (False, True):
+            dq, dk, dv, _ = oracle.attention_bwd(q, k, v, g, causal, scale, lib=lib, nthreads=1)
+            x = [t.double()[0, 0].numpy() for t in (q, k, v)]
+            gg = g.double()[0, 0].numpy()
+
+            def f(Q, K, V):
+                s = scale * Q @ K.T
+                if causal:
+                    s = np.where(np.tril(np.ones((Nq, Nk), dtype=bool), Nk - Nq), s, -np.inf)
+                p = np.exp(s - s.max(1, keepdims=True))
+                p /= p.sum(1, keepdims=True)
+                return float((gg * (p @ V)).sum())
+
+            rng = np.random.default_rng(9)
+            for which, grad in enumerate((dq, dk, dv)):
+                e = rng.standard_normal(x[which].shape)
+                h = 1e-5
+                plus = [t.copy() for t in x]
+                minus = [t.copy() for t in x]
+                plus[which] += h * e
+                minus[which] -= h * e
+                fd = (f(*plus) - f(*minus)) / (2 * h)
+                if abs(fd - float((grad[0, 0] * e).sum())) > 1e-7 * max(1.0, abs(fd)):
+                    return False
+        return True
+    check("finite_differences", finite_differences)
+
+    def d_matches_forward_oracle():
+        # D_i = dO_i . O_i with O from the forward oracle
+        q, k, v, g = _case(1, 2, 40, 40, 64, 509)
+        _, _, _, dsum = oracle.attention_bwd(q, k, v, g, True, 0.125, lib=lib, nthreads=2)
+        o, _ = oracle.attention(q, k, v, True, 0.125, nthreads=2)
+        return np.allclose(dsum, (o * g.double().numpy()).sum(-1), rtol=0, atol=1e-12)
+    check("d_matches_forward_oracle", d_matches_forward_oracle)
+    return fails
+
+
+def test_pin_suite_passes():
+    assert _pins(None) == []
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,d,causal", [
+    (1, 1, 1, 1, 64, True), (1, 1, 1, 1, 64, False), (1, 2, 1, 300, 128, True),
+    (2, 1, 70, 70, 128, True), (1, 1, 130, 130, 64, False)])
+def test_matches_autograd_float64(B, H, Nq, Nk, d, causal):
+    q, k, v, g = _case(B, H, Nq, Nk, d, 600 + Nq + Nk + d)
+    scale = 1.0 / math.sqrt(d)
+    dq, dk, dv, dsum = oracle.attention_bwd(q, k, v, g, causal, scale)
+    rq, rk, rv, o = _autograd64(q, k, v, g, causal, scale)
+    np.testing.assert_allclose(dq, rq, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk, rk, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv, rv, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dsum, (o * g.double().numpy()).sum(-1), rtol=0, atol=1e-12)
+
+
+def test_single_key_has_no_logit_gradient():
+    # one key: P = 1 whatever the logits, so dQ = dK = 0 and dV = sum_i dO_i
+    q, k, v, g = _case(1, 1, 17, 1, 64, 700)
+    dq, dk, dv, dsum = oracle.attention_bwd(q, k, v, g, False, 0.125)
+    assert np.abs(dq).max() == 0 and np.abs(dk).max() == 0
+    np.testing.assert_allclose(dv[0, 0, 0], g.double().numpy()[0, 0].sum(0), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dsum[0, 0], g.double().numpy()[0, 0] @ v.double().numpy()[0, 0, 0],
+                               rtol=0, atol=1e-13)
+
+
+def test_rejects_bad_arguments():
+    q, k, v, g = _case(1, 1, 8, 4, 16, 701)
+    with pytest.raises(RuntimeError):
+        oracle.attention_bwd(q, k, v, g, True, 0.1)  # causal with Nq > Nk
+    with pytest.raises(RuntimeError):
+        oracle.attention_bwd(q, k, v, g, False, float("nan"))
+    with pytest.raises(ValueError):
+        oracle.attention_bwd(q, k, v, g[:, :, :4], False, 0.1)
+
+
+MUTANTS = {
+    "dropped_d_term": ("const double ds = P[j] * (dP[j] - Di);", "const double ds = P[j] * dP[j];"),
+    "d_sign_flipped": ("const double ds = P[j] * (dP[j] - Di);",
+                       "const double ds = P[j] * (dP[j] + Di);"),
+    "dq_without_scale": ("dq[i * d + t] += c->scale * ds * widen(k[j * d + t]);",
+                         "dq[i * d + t] += ds * widen(k[j * d + t]);"),
+    "dk_without_scale": ("dk[j * d + t] += c->scale * ds * qi[t];", "dk[j * d + t] += ds * qi[t];"),
+    "dq_from_values": ("dq[i * d + t] += c->scale * ds * widen(k[j * d + t]);",
+                       "dq[i * d + t] += c->scale * ds * widen(v[j * d + t]);"),
+    "dk_from_upstream": ("dk[j * d + t] += c->scale * ds * qi[t];",
+                         "dk[j * d + t] += c->scale * ds * gi[t];"),
+    "dv_from_queries": ("dv[j * d + t] += P[j] * gi[t];", "dv[j * d + t] += P[j] * qi[t];"),
+    "dv_with_ds": ("dv[j * d + t] += P[j] * gi[t];", "dv[j * d + t] += ds * gi[t];"),
+    "dp_against_keys": ("dot += gi[t] * widen(v[j * d + t]);", "dot += gi[t] * widen(k[j * d + t]);"),
+    "unnormalised_p": ("P[j] /= l;", "P[j] /= 1.0;"),
+    "causal_excludes_diagonal": ("c->causal ? i + (Nk - Nq) + 1 : Nk",
+                                 "c->causal ? (i + (Nk - Nq) > 0 ? i + (Nk - Nq) : 1) : Nk"),
+    "causal_top_left_aligned": ("c->causal ? i + (Nk - Nq) + 1 : Nk", "c->causal ? i + 1 : Nk"),
+    "value_head_stride_of_queries": ("*v = c->v + bh * Nk * d;", "*v = c->v + bh * Nq * d;"),
+    "d_from_first_key_only": ("Di += P[j] * dP[j];", "Di += (j == 0) ? dP[j] : 0.0;"),
+}
+
+
+@pytest.fixture(scope="module")
+def bwd_source():
+    with open(os.path.join(os.path.dirname(oracle.__file__), "attn_bwd_oracle.c")) as f:
+        return f.read()
+
+
+def _build(src_text, path):
+    with open(path + ".c", "w") as f:
+        f.write(src_text)
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+                           "-o", path, path + ".c", "-lm"])
+    return oracle_impl.load_bwd_library(path)
+
+
+def test_unmodified_source_passes_the_suite(bwd_source, tmp_path):
+    assert _pins(_build(bwd_source, str(tmp_path / "libbwd_clean.so"))) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, bwd_source, tmp_path):
+    old, new = MUTANTS[name]
+    assert bwd_source.count(old) == 1, "mutation site not found: %r" % old
+    lib = _build(bwd_source.replace(old, new), str(tmp_path / ("libbwd_%s.so" % name)))
+    assert _pins(lib), "no pin caught mutant %s" % name
