@@ -22,8 +22,8 @@ ATTN_OK = 0
 STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_NULL_PTR", 2: "ATTN_BAD_SHAPE", 3: "ATTN_UNSUPPORTED_D",
                 4: "ATTN_BAD_SCALE", 5: "ATTN_MISALIGNED", 6: "ATTN_ALIAS", 7: "ATTN_HIP",
                 8: "ATTN_BAD_WORKSPACE"}
-EXPORTS = ("attn_fwd", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_bytes", "attn_status_string",
-           "attn_last_hip_error")
+EXPORTS = ("attn_fwd", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_bytes", "attn_bwd",
+           "attn_bwd_workspace_bytes", "attn_status_string", "attn_last_hip_error")
 
 _lib = None
 
@@ -56,6 +56,11 @@ def load():
                                      i64, p, i64, p]
     lib.attn_fwd_splitkv_workspace_bytes.restype = i64
     lib.attn_fwd_splitkv_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
+    lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_bwd.argtypes = [p, p, p, p, p, p, p, p, p, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float,
+                             p, i64, p]
+    lib.attn_bwd_workspace_bytes.restype = i64
+    lib.attn_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_status_string.argtypes = [ctypes.c_int]
     lib.attn_last_hip_error.restype = ctypes.c_int
@@ -187,3 +192,58 @@ def attention_splitkv(q, k, v, num_splits, causal=False, scale=None, with_lse=Tr
     attn_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, num_splits, workspace,
                      max(nbytes, 0) if workspace is not None else 0, stream)
     return o, lse
+
+
+def bwd_workspace_bytes(B, H, N, d):
+    """attn_bwd_workspace_bytes of include/attn.h (-1: invalid arguments)."""
+    return load().attn_bwd_workspace_bytes(int(B), int(H), int(N), int(d))
+
+
+def attn_bwd_status(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, causal, scale, workspace,
+                    workspace_bytes, stream=None):
+    """Call attn_bwd and return its status code (0 = ATTN_OK).
+
+    q, k, v, o, dout, dq, dk, dv: bf16 [B, H, N, d]; lse: fp32 [B, H, N] (the
+    forward pass's); workspace: a device tensor, a raw pointer, or None.
+    Tensors are checked against the shapes; raw pointers are the caller's
+    responsibility.
+    """
+    shape = (int(B), int(H), int(N), int(d))
+    for x, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (dq, "dq"), (dk, "dk"),
+                    (dv, "dv")):
+        _check(x, name, shape, torch.bfloat16)
+    _check(lse, "lse", shape[:3], torch.float32)
+    lib = load()
+    return lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                        _ptr(dv), int(B), int(H), int(N), int(d), 1 if causal else 0, float(scale),
+                        _ptr(workspace), int(workspace_bytes), _stream(stream))
+
+
+def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, causal, scale, workspace, workspace_bytes,
+             stream=None):
+    """attn_bwd of include/attn.h; raises AttnError on a nonzero status."""
+    st = attn_bwd_status(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, causal, scale, workspace,
+                         workspace_bytes, stream)
+    if st != ATTN_OK:
+        raise AttnError(st, load().attn_last_hip_error() if st == 7 else 0)
+
+
+def attention_bwd(q, k, v, o, lse, dout, causal=False, scale=None, stream=None, workspace=None):
+    """Allocate dQ, dK, dV (and the workspace unless given) and run attn_bwd
+    on torch's current stream.
+
+    q, k, v, o, dout: contiguous bf16 CUDA tensors [B, H, N, d]; lse: the
+    forward pass's fp32 [B, H, N].  Returns (dq, dk, dv).
+    """
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = d ** -0.5
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    nbytes = bwd_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, causal, scale, workspace,
+             workspace.numel() * workspace.element_size(), stream)
+    return dq, dk, dv

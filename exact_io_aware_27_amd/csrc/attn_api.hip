@@ -167,3 +167,93 @@ extern "C" int64_t attn_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_
         return -1;
     return bytes;
 }
+
+extern "C" int64_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d)
+{
+    int64_t BH, rows, bytes;
+    if (B < 0 || H < 0 || N < 0 || (d != 64 && d != 128) || !mul_ok(B, H, &BH) || !mul_ok(BH, N, &rows) ||
+        !mul_ok(rows, 8, &bytes))
+        return -1;
+    return bytes;
+}
+
+extern "C" int attn_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                        const void *dout, void *dq, void *dk, void *dv, int64_t B, int64_t H, int64_t N,
+                        int64_t d, int causal, float scale, void *workspace, int64_t workspace_bytes,
+                        void *stream)
+{
+    // 1. Shapes.
+    int64_t BH, rows, elems, bytes, vec_bytes, ws_need;
+    if (B < 0 || H < 0 || N < 0 || !mul_ok(B, H, &BH) || !mul_ok(BH, N, &rows))
+        return ATTN_BAD_SHAPE;
+    // 2. Head dimension.
+    if (d != 64 && d != 128)
+        return ATTN_UNSUPPORTED_D;
+    if (!mul_ok(rows, d, &elems) || !mul_ok(elems, 2, &bytes) || !mul_ok(rows, 4, &vec_bytes) ||
+        !mul_ok(rows, 8, &ws_need))
+        return ATTN_BAD_SHAPE;
+    if (N * d >= (int64_t(1) << 31))  // in-head offsets are 32-bit
+        return ATTN_BAD_SHAPE;
+    if (rows > 0 && attn_bwd_workgroups(BH, N) > INT32_MAX)
+        return ATTN_BAD_SHAPE;
+    // 3. Scale.
+    if (!std::isfinite(scale))
+        return ATTN_BAD_SCALE;
+    // 4. Empty problem.
+    if (rows == 0)
+        return ATTN_OK;
+    // 5. Pointers.
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
+        return ATTN_NULL_PTR;
+    // 6. Alignment.
+    const auto mis16 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; };
+    if (mis16(q) || mis16(k) || mis16(v) || mis16(o) || mis16(dout) || mis16(dq) || mis16(dk) || mis16(dv) ||
+        (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
+        return ATTN_MISALIGNED;
+    // 7. Outputs must not overlap any input or each other (inputs may alias
+    //    one another).
+    const void *ins[6] = {q, k, v, o, dout, lse};
+    const int64_t in_bytes[6] = {bytes, bytes, bytes, bytes, bytes, vec_bytes};
+    void *outs[3] = {dq, dk, dv};
+    for (int i = 0; i < 3; ++i) {
+        for (int j = 0; j < 6; ++j)
+            if (overlaps(outs[i], bytes, ins[j], in_bytes[j]))
+                return ATTN_ALIAS;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlaps(outs[i], bytes, outs[j], bytes))
+                return ATTN_ALIAS;
+    }
+    // 8. Workspace.
+    if (!workspace || mis16(workspace) || workspace_bytes < ws_need)
+        return ATTN_BAD_WORKSPACE;
+    for (int j = 0; j < 6; ++j)
+        if (overlaps(workspace, ws_need, ins[j], in_bytes[j]))
+            return ATTN_BAD_WORKSPACE;
+    for (int i = 0; i < 3; ++i)
+        if (overlaps(workspace, ws_need, outs[i], bytes))
+            return ATTN_BAD_WORKSPACE;
+
+    AttnBwdLaunch a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.dout = dout;
+    a.lse = lse;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.workspace = workspace;
+    a.BH = BH;
+    a.N = N;
+    a.d = d;
+    a.causal = causal != 0;
+    a.scale = scale;
+    a.stream = static_cast<hipStream_t>(stream);
+    const hipError_t err = attn_bwd_launch(a);
+    if (err != hipSuccess) {
+        g_last_hip_error = static_cast<int>(err);
+        return ATTN_HIP;
+    }
+    return ATTN_OK;
+}

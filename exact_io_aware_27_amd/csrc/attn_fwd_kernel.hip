@@ -67,34 +67,18 @@
 
 #include <type_traits>
 
+#include "attn_common.h"
 #include "attn_launch.h"
 
 namespace attn_gfx950 {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T *)(p))
-
-constexpr int kWave = 64;
 constexpr int kRowsPerWave = 32;
 constexpr int kBrMin = 128;  // fewest query rows per workgroup (d = 64)
 constexpr int kBc = 64;      // keys per K/V tile (two 32-key blocks)
-constexpr int kXcds = 8;     // MI355X: 8 XCDs, workgroups dealt round-robin
-constexpr float kNegInf = -__builtin_inff();
 // A block's probabilities are taken against a reference max that may lag
 // the true running max by up to kRefSlack (log2 units): p <= 2^16.  A row
 // whose next block would exceed that moves the reference to its exact max.
 constexpr float kRefSlack = 16.f;
-// Buffer-resource word 3 for raw (unformatted, stride-0) 32-bit loads with
-// out-of-range offsets returning zero.
-constexpr int kBufferFlags = 0x00020000;
 
 // Workgroup shape per head dim.  d = 128: 8 waves (256 queries), one
 // workgroup per CU, two waves per SIMD from the same workgroup: each K/V
@@ -155,52 +139,6 @@ template <int D>
 __device__ __forceinline__ int v_offset(int r, int c)
 {
     return r * Tile<D>::kRowBytes + ((c ^ swz_v<D>(r)) << 4);
-}
-
-// v_permlane32_swap_b32 a, b exchanges lanes 32..63 of a with lanes 0..31 of
-// b.  Starting from a = b = x this leaves a = [x_lo, x_lo], b = [x_hi, x_hi],
-// so op(a, b) combines lane l with lane l^32 in every lane.  It is issued as
-// inline asm with two read-write operands: the compiler builtin's second
-// result gets dropped when both operands carry the same value.  The asm is
-// not volatile, so the scheduler may move it like any VALU instruction; the
-// s_nops cover the VALU-write to permlane-read hazard the compiler cannot see
-// inside the asm.
-__device__ __forceinline__ void half_swap(float &a, float &b)
-{
-    asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-}
-
-__device__ __forceinline__ float wave_half_max(float x)
-{
-    float a = x, b = x;
-    half_swap(a, b);
-    return fmaxf(a, b);
-}
-
-__device__ __forceinline__ float wave_half_sum(float x)
-{
-    float a = x, b = x;
-    half_swap(a, b);
-    return a + b;
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
-{
-    const f32x2 f = {lo, hi};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));  // RNE
-}
-
-// Logical workgroup order: XCD-major (consecutive logical indices share an
-// XCD, so the units of one head stay on one XCD), then head-major.
-__device__ __forceinline__ void unit_of(int wg, int n_wg, int n_units, int &bh, int &unit)
-{
-    const int xcd = wg % kXcds;
-    const int slot = wg / kXcds;
-    const int per = n_wg / kXcds;
-    const int extra = n_wg % kXcds;
-    const int lin = xcd * per + (xcd < extra ? xcd : extra) + slot;
-    bh = lin / n_units;
-    unit = lin % n_units;
 }
 
 // Kernel arguments.  Q, O, LSE: [BH][Nq](×d); K, V: [BH][Nk][d].  Under the
@@ -726,7 +664,6 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float *__restrict
     const int row = gid / kChunks, c = gid % kChunks;
     if (row >= rows)
         return;
-    constexpr float kLog2e = 1.44269504088896340736f;
     float m = kNegInf;
     for (int s = 0; s < S; ++s)
         m = fmaxf(m, LSEpart[(size_t)s * rows + row]);
@@ -772,7 +709,7 @@ static hipError_t launch(const AttnLaunch &a, int splits, int split_keys)
     k.n_splits = splits;
     k.split_keys = split_keys;
     k.n_wg = (int)(a.BH * (CAUSAL ? (k.nqt + 1) / 2 : k.nqt) * splits);
-    k.c_log2 = a.scale * 1.44269504088896340736f;
+    k.c_log2 = a.scale * kLog2e;
     hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, SPLIT>), dim3(k.n_wg), dim3(T::kThreads), 0, a.stream, k);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || !SPLIT)

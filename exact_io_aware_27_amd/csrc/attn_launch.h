@@ -1,5 +1,6 @@
 // attn_launch.h -- internal interface between the validating C ABI
-// (attn_api.hip) and the gfx950 kernels (attn_fwd_kernel.hip).  Not installed.
+// (attn_api.hip) and the gfx950 kernels (attn_fwd_kernel.hip,
+// attn_bwd_kernel.hip).  Not installed.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -33,3 +34,22 @@ int64_t attn_workgroups(int64_t BH, int64_t Nq, int64_t Nk, int64_t num_splits);
 
 // Enqueue the kernel(s); returns hipGetLastError() after the launches.
 hipError_t attn_launch(const AttnLaunch &a);
+
+// Arguments of one validated backward call (attn_bwd).  d is 64 or 128,
+// N * d is below 2^31 and the workgroup count fits in an int.
+struct AttnBwdLaunch {
+    const void *q, *k, *v, *o, *dout;  // [BH][N][d] bf16
+    const float *lse;                  // [BH][N], natural log
+    void *dq, *dk, *dv;                // [BH][N][d] bf16
+    void *workspace;                   // attn_bwd_workspace_bytes() bytes
+    int64_t BH, N, d;
+    bool causal;
+    float scale;
+    hipStream_t stream;
+};
+
+// Workgroups of each backward kernel (an upper bound over masks).
+int64_t attn_bwd_workgroups(int64_t BH, int64_t N);
+
+// Enqueue the two backward kernels; returns hipGetLastError() after them.
+hipError_t attn_bwd_launch(const AttnBwdLaunch &a);

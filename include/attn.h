@@ -1,6 +1,6 @@
 /*
- * attn.h -- C ABI of libattn.so: exact, fused attention forward pass on
- * AMD MI355X (gfx950).
+ * attn.h -- C ABI of libattn.so: exact, fused attention forward pass (and
+ * its gradients) on AMD MI355X (gfx950).
  *
  * What the call computes, for every batch b and head h:
  *
@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-/* Status codes returned by attn_fwd() and attn_fwd_splitkv(). */
+/* Status codes returned by attn_fwd(), attn_fwd_splitkv() and attn_bwd(). */
 enum attn_status {
     ATTN_OK = 0,
     ATTN_NULL_PTR = 1,      /* q, k, v or o is NULL (and the problem is not empty) */
@@ -57,9 +57,9 @@ enum attn_status {
     ATTN_MISALIGNED = 5,    /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
     ATTN_ALIAS = 6,         /* o or lse overlaps q, k or v, or o overlaps lse */
     ATTN_HIP = 7,           /* the kernel launch failed; see attn_last_hip_error() */
-    ATTN_BAD_WORKSPACE = 8  /* attn_fwd_splitkv: workspace NULL, not 16-byte aligned,
-                               smaller than attn_fwd_splitkv_workspace_bytes(), or
-                               overlapping q, k, v, o or lse */
+    ATTN_BAD_WORKSPACE = 8  /* attn_fwd_splitkv, attn_bwd: workspace NULL, not 16-byte
+                               aligned, smaller than the *_workspace_bytes() size, or
+                               overlapping a tensor of the call */
 };
 
 /*
@@ -133,11 +133,55 @@ ATTN_API int attn_fwd_splitkv(const void *q, const void *k, const void *v, void 
 ATTN_API int64_t attn_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t d,
                                           int64_t num_splits);
 
+/*
+ * attn_bwd -- gradients of attn_fwd: dQ, dK and dV for an upstream gradient
+ * dO, by recomputing the scores and probabilities tile by tile from the
+ * forward pass's LSE instead of storing them (recomputation paragraph of
+ * "FlashAttention evolution", letsgetai.github.io; "FlashAttention" concept
+ * page, compassingai.com, section 3).  With P_ij = exp(scale q_i . k_j -
+ * LSE_i) over the visible keys (the causal rule of attn_fwd) and
+ * D_i = dO_i . O_i:
+ *
+ *   dV_j = sum_i P_ij dO_i
+ *   dS_ij = P_ij (dO_i . v_j - D_i)
+ *   dQ_i = scale sum_j dS_ij k_j,   dK_j = scale sum_i dS_ij q_i
+ *
+ * (bf16 out; fp32 arithmetic, P and dS rounded to bf16 as matrix-core
+ * operands).  Results are deterministic: no atomics, the same bits for the
+ * same inputs.
+ *
+ * q, k, v  the forward call's inputs: bf16, contiguous [B][H][N][d].
+ * o, lse   the forward call's outputs for the same q, k, v, causal and scale
+ *          (lse is required here): o bf16 [B][H][N][d], lse fp32 [B][H][N].
+ * dout     dO, bf16 [B][H][N][d].
+ * dq, dk, dv  bf16 [B][H][N][d], fully overwritten.
+ * B, H, N, d, causal, scale, stream  as attn_fwd.
+ * workspace, workspace_bytes  device scratch of at least
+ *          attn_bwd_workspace_bytes(B, H, N, d) bytes (8 per row: the LSE in
+ *          log2 units and D), 16-byte aligned, owned by the caller; contents
+ *          on entry ignored, on return undefined; two calls in flight must
+ *          not share one.
+ * Ownership and asynchrony as attn_fwd (two kernels are enqueued).  Errors
+ * are checked in the order of attn_fwd: BAD_SHAPE, UNSUPPORTED_D, BAD_SCALE,
+ * (empty -> OK), NULL_PTR (any of the nine tensors), MISALIGNED (the bf16
+ * tensors and the workspace 16 bytes, lse 4 bytes), ALIAS (dq, dk or dv
+ * overlapping an input or each other; the inputs may alias one another),
+ * BAD_WORKSPACE (NULL, misaligned, too small, or overlapping any tensor).
+ */
+ATTN_API int attn_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+             const void *dout, void *dq, void *dk, void *dv,
+             int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+             void *workspace, int64_t workspace_bytes, void *stream);
+
+/* Bytes of workspace attn_bwd needs (8 B H N); -1 if the arguments are
+ * invalid (negative, d not 64/128, or the size overflows). */
+ATTN_API int64_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d);
+
 /* Static, human-readable name of a status code ("ATTN_OK", ...). */
 ATTN_API const char *attn_status_string(int status);
 
-/* The hipError_t of the last attn_fwd() call on this thread that returned
- * ATTN_HIP (0 if none has). */
+/* The hipError_t of the last call on this thread that returned ATTN_HIP
+ * (0 if none has). */
 ATTN_API int attn_last_hip_error(void);
 
 #ifdef __cplusplus

@@ -71,3 +71,44 @@ def gather_rows(x, rows):
     else:
         out = torch.gather(flat, 1, idx)
     return out.reshape(B, H, *out.shape[1:])
+
+
+# Gradients (attn_bwd).  Every element of dQ, dK and dV is one fp32-accumulated
+# sum of products of bf16 operands, one of which (P or dS) is itself rounded
+# to bf16 (unit roundoff u = 2^-8) before the product, and the sum is rounded
+# to bf16 on output.  Errors of a few u relative to the tensor's scale are the
+# arithmetic's own; a wrong mask, index or term is of the order of the
+# gradient itself.  Bar: mean|d| <= 1e-2 * mean|ref| (about 2.5 u) and
+# max|d| <= 2e-2 * max|ref| (about 5 u), per tensor and per head.  A head
+# whose exact gradient is zero (one key: dQ = dK = 0) is held to an absolute
+# 1e-5 instead: dS there is the difference of two fp32 sums of the same d
+# products of O(1) bf16 values, zero up to their rounding (d * 2^-24 * |terms|).
+GRAD_MEAN_REL = 1e-2
+GRAD_MAX_REL = 2e-2
+GRAD_ABS_FLOOR = 1e-5
+
+
+def compare_grad(g_gpu, ref):
+    """g_gpu: bf16 tensor [B, H, R, d]; ref: fp64 array of the same shape.
+    Worst per-head ratios of the error to the reference's scale (with the
+    absolute floor folded into the scale)."""
+    g = g_gpu.detach().float().cpu().numpy().astype(np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    B, H = ref.shape[:2]
+    g = g.reshape(B * H, -1)
+    ref = ref.reshape(B * H, -1)
+    diff = np.abs(g - ref)
+    scale_max = np.maximum(np.abs(ref).max(axis=1) * GRAD_MAX_REL, GRAD_ABS_FLOOR) / GRAD_MAX_REL
+    scale_mean = np.maximum(np.abs(ref).mean(axis=1) * GRAD_MEAN_REL, GRAD_ABS_FLOOR) / GRAD_MEAN_REL
+    return dict(
+        max_rel=float((diff.max(axis=1) / scale_max).max()) if diff.size else 0.0,
+        mean_rel=float((diff.mean(axis=1) / scale_mean).max()) if diff.size else 0.0,
+        max_abs=float(diff.max()) if diff.size else 0.0,
+        finite=bool(np.isfinite(g).all()),
+    )
+
+
+def assert_grad_parity(rep, what=""):
+    assert rep["finite"], "%s: non-finite gradient %s" % (what, rep)
+    assert rep["max_rel"] <= GRAD_MAX_REL, "%s: max|d| over 2e-2 max|ref|: %s" % (what, rep)
+    assert rep["mean_rel"] <= GRAD_MEAN_REL, "%s: mean|d| over 1e-2 mean|ref|: %s" % (what, rep)

@@ -30,7 +30,8 @@ def _declared():
 
 def test_header_declares_the_abi():
     assert set(_declared()) == {"attn_fwd", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_bytes",
-                                "attn_status_string", "attn_last_hip_error"}
+                                "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_string",
+                                "attn_last_hip_error"}
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -122,6 +123,46 @@ def test_splitkv_workspace_bytes(lib):
     assert f(2, 3, 7, 128, 1) == 0
     for bad in [(-1, 3, 7, 128, 4), (2, 3, -7, 128, 4), (2, 3, 7, 96, 4), (2, 3, 7, 128, 0),
                 (1 << 40, 1 << 20, 1 << 10, 128, 64)]:
+        assert f(*bad) == -1
+
+
+# fake gradient addresses for attn_bwd
+G, DQ, DK, DV = 0x70000000, 0x80000000, 0x90000000, 0xA0000000
+
+
+def _bwd(lib, q=Q, k=K, v=V, o=O, lse=L, g=G, dq=DQ, dk=DK, dv=DV, B=2, H=3, N=100, d=128, causal=1,
+         scale=0.1, ws=W, wsb=None):
+    if wsb is None:
+        wsb = lib.attn_bwd_workspace_bytes(B, H, N, d)
+    return lib.attn_bwd(q, k, v, o, lse, g, dq, dk, dv, B, H, N, d, causal, scale, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), 2), (dict(N=-1), 2), (dict(B=1 << 40, H=1 << 30), 2), (dict(N=1 << 24), 2),
+    (dict(d=96), 3), (dict(scale=float("nan")), 4), (dict(scale=float("inf")), 4),
+    (dict(B=0, q=None, dq=None, ws=None), 0), (dict(N=0, ws=None), 0),
+    (dict(q=None), 1), (dict(o=None), 1), (dict(lse=None), 1), (dict(g=None), 1),
+    (dict(dq=None), 1), (dict(dk=None), 1), (dict(dv=None), 1),
+    (dict(g=G + 8), 5), (dict(dk=DK + 2), 5), (dict(lse=L + 2), 5), (dict(o=O + 4), 5),
+    (dict(dq=Q), 6), (dict(dk=O + 64), 6), (dict(dv=G), 6), (dict(dq=L - 64), 6),
+    (dict(dk=DQ + 1024), 6), (dict(dv=DK), 6),
+    (dict(ws=None), 8), (dict(ws=W + 8), 8), (dict(wsb=100), 8), (dict(ws=DV), 8),
+    (dict(ws=L), 8), (dict(ws=G + 256), 8),
+])
+def test_bwd_argument_errors_before_any_hip_call(lib, kw, status):
+    assert _bwd(lib, **kw) == status
+
+
+def test_bwd_inputs_may_alias_each_other(lib):
+    # shared inputs are legal; the only error left is the misaligned dv
+    assert _bwd(lib, k=Q, v=Q, o=Q, g=Q, dv=DV + 4) == 5
+
+
+def test_bwd_workspace_bytes(lib):
+    f = lib.attn_bwd_workspace_bytes
+    assert f(2, 3, 100, 128) == 2 * 3 * 100 * 8
+    assert f(1, 1, 0, 64) == 0
+    for bad in [(-1, 3, 7, 128), (2, 3, -7, 128), (2, 3, 7, 96), (1 << 40, 1 << 20, 1 << 10, 128)]:
         assert f(*bad) == -1
 
 
