@@ -28,7 +28,7 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "attn fwd TFLOP/s + % of bf16 MFMA peak, 1 GPU, N=8192 d=128 causal"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_long_causal_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_io_aware_27_amd", "csrc", f)
-                  for f in ("attn_fwd_kernel.hip", "attn_launch.h")]
+                  for f in ("attn_fwd_kernel.hip", "attn_common.h", "attn_launch.h")]
 
 
 def kernel_hash():
@@ -211,6 +211,87 @@ def bench_splitkv(args):
     return 0
 
 
+def bench_bwd(args):
+    """One JSON line for the backward pass (attn_bwd: the dQ kernel, then the
+    dK/dV kernel) on a workload of WORKLOADS.  One step is one attn_bwd call
+    over the whole batch; O and LSE come from one attn_fwd call before the
+    timed region.  Counted work is the five products of the gradient
+    definition (S, dP, dV, dK, dQ: 10*B*H*N^2*d, halved when causal); the
+    kernels recompute S and dP in both passes (seven products), which the
+    count does not credit."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from exact_io_aware_27_amd import attn, inputs
+
+    attn.load()
+    w = {x.name: x for x in inputs.WORKLOADS}[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = inputs.workload_qkv(w)
+    g = inputs.make_grad_out(w.B, w.H, w.N, w.d, seed=w.seed + 104729)
+    qd, kd, vd, gd = q.to(dev), k.to(dev), v.to(dev), g.to(dev)
+    stream = torch.cuda.current_stream(dev)
+    od, lsed = attn.attention(qd, kd, vd, causal=w.causal, scale=w.scale, stream=stream)
+    dq, dk, dv = (torch.empty_like(qd) for _ in range(3))
+    nb = attn.bwd_workspace_bytes(w.B, w.H, w.N, w.d)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+
+    def step():
+        attn.attn_bwd(qd, kd, vd, od, lsed, gd, dq, dk, dv, w.B, w.H, w.N, w.d, w.causal, w.scale, ws, nb,
+                      stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    flops = 2.5 * w.flops
+    tflops = flops / (ms * 1e-3) / 1e12
+    out = {"metric": "attn bwd TFLOP/s (5-product count) + % of bf16 MFMA peak, 1 GPU", "value": round(tflops, 2),
+           "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": w.describe() + " backward", "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                      "causal": w.causal, "scale": w.scale, "seed": w.seed},
+           "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": round(PEAK_BF16_TFLOPS, 1),
+                        "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                        "kernels": "attn_bwd_dq_kernel + attn_bwd_dkdv_kernel, back to back"}}
+    if args.cpu_heads > 0:
+        # the oracle on whole heads (dK and dV need every query of a head)
+        heads = [(b, h) for b in range(w.B) for h in range(w.H)][:args.cpu_heads]
+        threads = min(len(heads), oracle.oracle.default_threads())
+        sel = torch.tensor([b * w.H + h for b, h in heads])
+
+        def pick(x):
+            return x.reshape(w.B * w.H, *x.shape[2:])[sel].unsqueeze(0).contiguous()
+
+        t0 = time.perf_counter()
+        rq, rk, rv, _ = oracle.attention_bwd(pick(q), pick(k), pick(v), pick(g), w.causal, w.scale,
+                                             nthreads=threads)
+        dt = time.perf_counter() - t0
+        head_flops = 2.5 * w.flops / (w.B * w.H)
+        out["cpu_baseline"] = {"value": head_flops * len(heads) / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+                               "kind": "oracle",
+                               "sample": "%d whole head(s) of the workload, every query and key; %.3g counted "
+                                         "flops in %.1f s" % (len(heads), head_flops * len(heads), dt)}
+        rel = {}
+        for name, x, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+            xs = pick(x.cpu()).double().numpy()
+            rel[name + "_max_rel"] = float(np.abs(xs - ref).max() / max(np.abs(ref).max(), 1e-30))
+        out["parity_sampled_heads"] = dict(heads=len(heads), **rel)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -223,6 +304,9 @@ def main():
     ap.add_argument("--splitkv", default=None,
                     help="measure attn_fwd_splitkv on a workload of exact_io_aware_27_amd.inputs.SPLITKV_WORKLOADS")
     ap.add_argument("--splits", type=int, default=0, help="key ranges for --splitkv (0: the workload's)")
+    ap.add_argument("--bwd", action="store_true", help="measure the backward pass (attn_bwd) on --workload")
+    ap.add_argument("--cpu-heads", type=int, default=1,
+                    help="--bwd: whole heads in the oracle's CPU-baseline sample (0: skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (HBM counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -242,6 +326,8 @@ def main():
 
     if args.splitkv:
         return bench_splitkv(args)
+    if args.bwd:
+        return bench_bwd(args)
 
     import torch
 
