@@ -124,6 +124,29 @@ def make_grad_out(B, H, Nq, d, seed, sigma=1.0):
     return (torch.randn((B, H, Nq, d), generator=g, dtype=torch.float32) * sigma).to(torch.bfloat16)
 
 
+def make_signs(d, seed):
+    """The random signs of incoherent processing: d values +-1 (float32)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    return (torch.randint(0, 2, (d,), generator=g) * 2 - 1).to(torch.float32)
+
+
+def make_qkv_outliers(B, H, N, d, seed, frac=1e-3, outlier_sigma=10.0):
+    """Q, K, V as make_qkv (standard normal), then a fraction `frac` of the
+    entries of each, at seeded positions, replaced by normals of standard
+    deviation outlier_sigma: the outlier-heavy input on which per-tensor FP8
+    loses accuracy.  CPU bfloat16."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    out = []
+    for _ in range(3):
+        x = torch.randn((B, H, N, d), generator=g, dtype=torch.float32)
+        hit = torch.rand((B, H, N, d), generator=g) < frac
+        x = torch.where(hit, torch.randn((B, H, N, d), generator=g) * outlier_sigma, x)
+        out.append(x.to(torch.bfloat16))
+    return tuple(out)
+
+
 def make_qkv(B, H, N, d, seed, sigma_qk=1.0, sigma_v=1.0):
     """Q, K, V as CPU bfloat16 tensors [B, H, N, d], drawn in that order."""
     g = torch.Generator(device="cpu")

@@ -10,6 +10,9 @@ library never imports it; the two share no code.
 - ``attention_bwd``: the gradients dQ, dK, dV of that definition for an
   upstream gradient dO, in C (``attn_bwd_oracle.c``), fp64, one thread per
   head.
+- ``fp8_oracle``: FP8 (E4M3) block quantization with incoherent processing
+  (random-sign Hadamard rotation of Q and K) and the FP8 attention method
+  emulated in NumPy, for the FP8 path.
 - ``online``: the pages' tiled recurrence (running max m and running sum l)
   and the two-block merge identity, in NumPy fp64, used to pin the reading
   of the recurrence against the definition.

@@ -1,0 +1,135 @@
+"""Pins of the FP8 oracle (oracle/fp8_oracle.py) to things other than itself.
+
+  E4M3 rounding        -> PyTorch's float8_e4m3fn conversion, the format's
+                          fixed points (448, 2^-9, ties to even)
+  Hadamard / FWHT      -> H H^T = d I, the dense product x @ H, exact on
+                          integers; rotation keeps Q K^T up to the factor d
+  block exponents      -> the defining inequality, brute force
+  quantize / dequant   -> E4M3's relative error bound per element
+  attention_fp64       -> the pinned C oracle on bf16 inputs
+  P-rounding noise     -> the actual E4M3 rounding of P, measured
+  the pages' claim     -> block quantization with incoherent processing has
+                          lower error than per-tensor FP8 on outlier-heavy input
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import fp8_oracle as f8
+from exact_io_aware_27_amd import inputs
+
+
+def test_e4m3_round_matches_torch_float8_e4m3fn():
+    rng = np.random.default_rng(1)
+    x = np.concatenate([
+        rng.uniform(-448, 448, 20000),
+        rng.standard_normal(20000) * 2.0 ** rng.integers(-12, 8, 20000),
+        np.arange(-448, 449, 0.5),                      # many exact ties
+        np.ldexp(np.arange(0, 64), -10),                # subnormal ties at 2^-10 steps
+    ])
+    x = x[np.abs(x) <= 448]
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).double().numpy()
+    np.testing.assert_array_equal(f8.e4m3_round(x), ref)
+
+
+def test_e4m3_fixed_points():
+    assert f8.e4m3_round(448.0) == 448.0 and f8.e4m3_round(-448.0) == -448.0
+    assert f8.e4m3_round(2.0 ** -9) == 2.0 ** -9 and f8.e4m3_round(2.0 ** -10) == 0.0
+    assert f8.e4m3_round(1.0625) == 1.0 and f8.e4m3_round(1.1875) == 1.25  # ties to even
+    assert f8.e4m3_round(17.0) == 16.0 and f8.e4m3_round(19.0) == 20.0
+    with pytest.raises(ValueError):
+        f8.e4m3_round(449.0)
+
+
+def test_hadamard_and_fwht():
+    for d in (2, 8, 64, 128):
+        H = f8.hadamard(d)
+        np.testing.assert_array_equal(H @ H.T, d * np.eye(d))
+    rng = np.random.default_rng(2)
+    xi = rng.integers(-50, 50, (5, 128)).astype(np.float32)  # small integers: exact in fp32
+    np.testing.assert_array_equal(f8.fwht_f32(xi), xi.astype(np.float64) @ f8.hadamard(128))
+    xr = rng.standard_normal((5, 128)).astype(np.float32)
+    np.testing.assert_allclose(f8.fwht_f32(xr), xr.astype(np.float64) @ f8.hadamard(128), atol=1e-4)
+
+
+def test_rotation_keeps_scores_up_to_the_factor_d():
+    q, k, _ = inputs.make_qkv(1, 1, 20, 128, seed=11)
+    s = inputs.make_signs(128, seed=12).numpy().astype(np.float64)
+    H = f8.hadamard(128)
+    qd, kd = q.double().numpy()[0, 0], k.double().numpy()[0, 0]
+    np.testing.assert_allclose(((qd * s) @ H) @ ((kd * s) @ H).T, 128 * qd @ kd.T, rtol=1e-12, atol=1e-9)
+
+
+def test_block_exponent_is_the_smallest_that_fits():
+    rng = np.random.default_rng(3)
+    for amax in np.concatenate([rng.uniform(1e-6, 1e6, 2000), [448.0, 224.0, 896.0, 1.75, 2.0 ** -20]]):
+        E = f8.block_exponent(amax)
+        assert amax <= 448 * 2.0 ** E and amax > 448 * 2.0 ** (E - 1)
+    assert f8.block_exponent(0.0) == 0
+
+
+def test_block_quantize_error_bound_and_ragged_tail():
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal((2, 150, 64)) * np.exp(rng.uniform(-3, 3, (2, 150, 1)))).astype(np.float32)
+    codes, exps = f8.block_quantize(x)
+    assert exps.shape == (2, 3)
+    xh = f8.dequantize(codes, exps)
+    scale = np.repeat(2.0 ** exps, 64, axis=-1)[:, :150, None]
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * scale)  # half a quantum, normal or subnormal
+    assert np.all(np.abs(xh - x) <= bound * (1 + 1e-12))
+    for b in range(3):
+        amax = np.abs(codes[:, b * 64:(b + 1) * 64]).max(axis=(1, 2))
+        assert np.all((amax > 224) & (amax <= 448))
+
+
+def test_attention_fp64_matches_the_c_oracle():
+    q, k, v = inputs.make_qkv(1, 2, 90, 64, seed=13)
+    for causal in (False, True):
+        o, lse = f8.attention_fp64(q.double().numpy(), k.double().numpy(), v.double().numpy(), causal, 0.125)
+        oc, lc = oracle.attention(q, k, v, causal, 0.125)
+        np.testing.assert_allclose(o, oc, atol=1e-12)
+        np.testing.assert_allclose(lse, lc, atol=1e-12)
+
+
+def test_p_rounding_noise_model_matches_actual_rounding():
+    # O with P rounded to E4M3 (relative to the row max, divided by the
+    # unrounded sum) against the exact O: the squared error over sigma^2
+    # averages near 1 when the model is right
+    q, k, v = inputs.make_qkv(1, 2, 300, 64, seed=14)
+    qd, kd, vd = (x.double().numpy() for x in (q, k, v))
+    o, _, sigma = f8.attention_fp64(qd, kd, vd, True, 0.125, p_rounding=True)
+    prep = {"q": qd, "k": kd, "v": vd, "qk_factor": 1.0}
+    o8, _ = f8.attention_fp8(prep, True, 0.125)
+    z = ((o8 - o) / np.maximum(sigma, 1e-30))[:, :, 1:]  # row 0 sees one key: P = 1 exactly
+    assert 0.3 < float(np.mean(z ** 2)) < 1.5, float(np.mean(z ** 2))
+
+
+def test_block_and_incoherent_processing_beat_per_tensor_fp8_on_outliers():
+    """The pages report that FP8 with block quantization and incoherent
+    processing has 2.6x lower error than per-tensor FP8.  On outlier-heavy
+    synthetic input the oracle's FP8 emulation reproduces the direction and
+    comparable size of that gain (1% of entries with standard deviation 10).
+    With power-of-two scales and a floating-point format, per-block scaling
+    alone changes nothing here (no value leaves E4M3's normal range); the gain
+    is the rotation's."""
+    B, H, N, d = 1, 2, 256, 128
+    q, k, v = inputs.make_qkv_outliers(B, H, N, d, seed=15, frac=1e-2)
+    scale = 1 / math.sqrt(d)
+    ref, _ = oracle.attention(q, k, v, False, scale)
+    signs = inputs.make_signs(d, seed=16).numpy()
+
+    def rmse(prep):
+        o, _ = f8.attention_fp8(prep, False, scale)
+        return float(np.sqrt(np.mean((o - ref) ** 2)))
+
+    per_tensor = rmse(f8.prepare_fp8(q, k, v, per_tensor=True))
+    blocked = rmse(f8.prepare_fp8(q, k, v))
+    both = rmse(f8.prepare_fp8(q, k, v, signs=signs))
+    print("RMSE per-tensor %.4g, block %.4g, block + incoherent %.4g (ratio %.2f)"
+          % (per_tensor, blocked, both, per_tensor / both))
+    assert both < blocked <= per_tensor * 1.0001
+    assert per_tensor / both > 1.5
