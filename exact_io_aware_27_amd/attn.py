@@ -21,9 +21,10 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so"
 ATTN_OK = 0
 STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_NULL_PTR", 2: "ATTN_BAD_SHAPE", 3: "ATTN_UNSUPPORTED_D",
                 4: "ATTN_BAD_SCALE", 5: "ATTN_MISALIGNED", 6: "ATTN_ALIAS", 7: "ATTN_HIP",
-                8: "ATTN_BAD_WORKSPACE"}
+                8: "ATTN_BAD_WORKSPACE", 9: "ATTN_BAD_ARGUMENT"}
 EXPORTS = ("attn_fwd", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_bytes", "attn_bwd",
-           "attn_bwd_workspace_bytes", "attn_status_string", "attn_last_hip_error")
+           "attn_bwd_workspace_bytes", "attn_fp8_padded_rows", "attn_fp8_quantize", "attn_fwd_fp8",
+           "attn_status_string", "attn_last_hip_error")
 
 _lib = None
 
@@ -61,6 +62,12 @@ def load():
                              p, i64, p]
     lib.attn_bwd_workspace_bytes.restype = i64
     lib.attn_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    lib.attn_fp8_padded_rows.restype = i64
+    lib.attn_fp8_padded_rows.argtypes = [i64]
+    lib.attn_fp8_quantize.restype = ctypes.c_int
+    lib.attn_fp8_quantize.argtypes = [p, i64, i64, i64, i64, ctypes.c_int, p, p, p, p]
+    lib.attn_fwd_fp8.restype = ctypes.c_int
+    lib.attn_fwd_fp8.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float, p]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_status_string.argtypes = [ctypes.c_int]
     lib.attn_last_hip_error.restype = ctypes.c_int
@@ -247,3 +254,85 @@ def attention_bwd(q, k, v, o, lse, dout, causal=False, scale=None, stream=None, 
     attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, causal, scale, workspace,
              workspace.numel() * workspace.element_size(), stream)
     return dq, dk, dv
+
+
+def fp8_padded_rows(N):
+    """attn_fp8_padded_rows of include/attn.h: N rounded up to 64."""
+    return load().attn_fp8_padded_rows(int(N))
+
+
+def sign_bits(signs):
+    """+-1 signs [128] -> the 4-word host bit array attn_fp8_quantize takes
+    (bit c set: sign of column c is -1)."""
+    neg = [float(x) < 0 for x in (signs.tolist() if hasattr(signs, "tolist") else signs)]
+    if len(neg) != 128:
+        raise ValueError("signs must hold 128 values")
+    words = (ctypes.c_uint32 * 4)()
+    for c, is_neg in enumerate(neg):
+        if is_neg:
+            words[c // 32] |= 1 << (c % 32)
+    return words
+
+
+def fp8_quantize_status(x, B, H, N, d, transpose, signs, out, exps, stream=None):
+    """Call attn_fp8_quantize and return its status.  signs: None or +-1 [128]."""
+    lib = load()
+    bits = None if signs is None else sign_bits(signs)
+    return lib.attn_fp8_quantize(_ptr(x), int(B), int(H), int(N), int(d), 1 if transpose else 0,
+                                 None if bits is None else ctypes.cast(bits, ctypes.c_void_p),
+                                 _ptr(out), _ptr(exps), _stream(stream))
+
+
+def fp8_quantize(x, transpose=False, signs=None, stream=None):
+    """Quantize a contiguous bf16 CUDA tensor [B, H, N, 128] to FP8.
+
+    Returns (codes, exps): uint8 tensors [B, H, Np, 128] (or [B, H, 128, Np]
+    with transpose, in the kernel's key order) and [B, H, Np // 64].
+    """
+    B, H, N, d = x.shape
+    _check(x, "x", (B, H, N, d), torch.bfloat16)
+    Np = fp8_padded_rows(N)
+    shape = (B, H, d, Np) if transpose else (B, H, Np, d)
+    out = torch.empty(shape, dtype=torch.uint8, device=x.device)
+    exps = torch.empty((B, H, Np // 64), dtype=torch.uint8, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    st = fp8_quantize_status(x, B, H, N, d, transpose, signs, out, exps, stream)
+    if st != ATTN_OK:
+        raise AttnError(st, load().attn_last_hip_error() if st == 7 else 0)
+    return out, exps
+
+
+def attn_fwd_fp8_status(q8, k8, vt8, qe, ke, ve, o, lse, B, H, N, d, causal, scale, stream=None):
+    """Call attn_fwd_fp8 and return its status (0 = ATTN_OK)."""
+    _check(o, "o", (int(B), int(H), int(N), int(d)), torch.bfloat16)
+    _check(lse, "lse", (int(B), int(H), int(N)), torch.float32)
+    lib = load()
+    return lib.attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(vt8), _ptr(qe), _ptr(ke), _ptr(ve), _ptr(o), _ptr(lse),
+                            int(B), int(H), int(N), int(d), 1 if causal else 0, float(scale), _stream(stream))
+
+
+def attn_fwd_fp8(q8, k8, vt8, qe, ke, ve, o, lse, B, H, N, d, causal, scale, stream=None):
+    """attn_fwd_fp8 of include/attn.h; raises AttnError on a nonzero status."""
+    st = attn_fwd_fp8_status(q8, k8, vt8, qe, ke, ve, o, lse, B, H, N, d, causal, scale, stream)
+    if st != ATTN_OK:
+        raise AttnError(st, load().attn_last_hip_error() if st == 7 else 0)
+
+
+def attention_fp8(q, k, v, causal=False, scale=None, signs=None, stream=None):
+    """Quantize q, k (rotated with `signs` when given) and v, then run
+    attn_fwd_fp8 on torch's current stream.  q, k, v: contiguous bf16 CUDA
+    tensors [B, H, N, 128].  Returns (o, lse)."""
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = d ** -0.5
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    q8, qe = fp8_quantize(q, signs=signs, stream=stream)
+    k8, ke = fp8_quantize(k, signs=signs, stream=stream)
+    vt8, ve = fp8_quantize(v, transpose=True, stream=stream)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    eff = scale / d if signs is not None else scale  # the rotation multiplies Q K^T by d
+    attn_fwd_fp8(q8, k8, vt8, qe, ke, ve, o, lse, B, H, N, d, causal, eff, stream)
+    return o, lse

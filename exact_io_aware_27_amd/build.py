@@ -7,7 +7,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libattn.so")
-SOURCES = ["attn_api.hip", "attn_fwd_kernel.hip", "attn_bwd_kernel.hip"]
+SOURCES = ["attn_api.hip", "attn_fwd_kernel.hip", "attn_bwd_kernel.hip", "attn_fp8_kernel.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -44,6 +44,7 @@ extern "C" const char *attn_status_string(int status)
     case ATTN_ALIAS: return "ATTN_ALIAS";
     case ATTN_HIP: return "ATTN_HIP";
     case ATTN_BAD_WORKSPACE: return "ATTN_BAD_WORKSPACE";
+    case ATTN_BAD_ARGUMENT: return "ATTN_BAD_ARGUMENT";
     default: return "ATTN_UNKNOWN_STATUS";
     }
 }
@@ -251,6 +252,101 @@ extern "C" int attn_bwd(const void *q, const void *k, const void *v, const void 
     a.scale = scale;
     a.stream = static_cast<hipStream_t>(stream);
     const hipError_t err = attn_bwd_launch(a);
+    if (err != hipSuccess) {
+        g_last_hip_error = static_cast<int>(err);
+        return ATTN_HIP;
+    }
+    return ATTN_OK;
+}
+
+extern "C" int64_t attn_fp8_padded_rows(int64_t N) { return N < 0 ? -1 : attn_fp8_rows(N); }
+
+extern "C" int attn_fp8_quantize(const void *x, int64_t B, int64_t H, int64_t N, int64_t d, int transpose,
+                                 const uint32_t *sign_bits, void *out, void *exps, void *stream)
+{
+    int64_t BH, rows, np_rows, bytes, xbytes, nexp;
+    if (B < 0 || H < 0 || N < 0 || !mul_ok(B, H, &BH) || !mul_ok(BH, N, &rows))
+        return ATTN_BAD_SHAPE;
+    if (d != 128)
+        return ATTN_UNSUPPORTED_D;
+    const int64_t Np = attn_fp8_rows(N);
+    if (!mul_ok(BH, Np, &np_rows) || !mul_ok(np_rows, d, &bytes) || !mul_ok(rows, 2 * d, &xbytes) ||
+        N * d >= (int64_t(1) << 31) || Np * d >= (int64_t(1) << 31) || np_rows / 64 > INT32_MAX)
+        return ATTN_BAD_SHAPE;
+    nexp = np_rows / 64;
+    if (transpose && sign_bits)  // V is not rotated
+        return ATTN_BAD_ARGUMENT;
+    if (rows == 0)
+        return ATTN_OK;
+    if (!x || !out || !exps)
+        return ATTN_NULL_PTR;
+    if ((reinterpret_cast<uintptr_t>(x) & 15u) || (reinterpret_cast<uintptr_t>(out) & 15u))
+        return ATTN_MISALIGNED;
+    if (overlaps(out, bytes, x, xbytes) || overlaps(exps, nexp, x, xbytes) || overlaps(exps, nexp, out, bytes))
+        return ATTN_ALIAS;
+    AttnFp8Quantize q;
+    q.x = x;
+    q.out = out;
+    q.exps = exps;
+    q.sign_bits = sign_bits;
+    q.transpose = transpose != 0;
+    q.BH = BH;
+    q.N = N;
+    q.stream = static_cast<hipStream_t>(stream);
+    const hipError_t err = attn_fp8_quantize_launch(q);
+    if (err != hipSuccess) {
+        g_last_hip_error = static_cast<int>(err);
+        return ATTN_HIP;
+    }
+    return ATTN_OK;
+}
+
+extern "C" int attn_fwd_fp8(const void *q8, const void *k8, const void *vt8, const void *q_exps, const void *k_exps,
+                            const void *v_exps, void *o, float *lse, int64_t B, int64_t H, int64_t N, int64_t d,
+                            int causal, float scale, void *stream)
+{
+    int64_t BH, rows, np_rows, bytes, obytes, lse_bytes, nexp;
+    if (B < 0 || H < 0 || N < 0 || !mul_ok(B, H, &BH) || !mul_ok(BH, N, &rows))
+        return ATTN_BAD_SHAPE;
+    if (d != 128)
+        return ATTN_UNSUPPORTED_D;
+    const int64_t Np = attn_fp8_rows(N);
+    if (!mul_ok(BH, Np, &np_rows) || !mul_ok(np_rows, d, &bytes) || !mul_ok(rows, 2 * d, &obytes) ||
+        !mul_ok(rows, 4, &lse_bytes) || N * d >= (int64_t(1) << 31) || Np * d >= (int64_t(1) << 31) ||
+        attn_workgroups(BH, N, N, 1) > INT32_MAX)
+        return ATTN_BAD_SHAPE;
+    nexp = np_rows / 64;
+    if (!std::isfinite(scale))
+        return ATTN_BAD_SCALE;
+    if (rows == 0)
+        return ATTN_OK;
+    if (!q8 || !k8 || !vt8 || !q_exps || !k_exps || !v_exps || !o)
+        return ATTN_NULL_PTR;
+    const auto mis16 = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; };
+    if (mis16(q8) || mis16(k8) || mis16(vt8) || mis16(o) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+        return ATTN_MISALIGNED;
+    const void *ins[6] = {q8, k8, vt8, q_exps, k_exps, v_exps};
+    const int64_t in_bytes[6] = {bytes, bytes, bytes, nexp, nexp, nexp};
+    for (int j = 0; j < 6; ++j)
+        if (overlaps(o, obytes, ins[j], in_bytes[j]) || (lse && overlaps(lse, lse_bytes, ins[j], in_bytes[j])))
+            return ATTN_ALIAS;
+    if (lse && overlaps(lse, lse_bytes, o, obytes))
+        return ATTN_ALIAS;
+    AttnFp8Launch a;
+    a.q8 = q8;
+    a.k8 = k8;
+    a.vt8 = vt8;
+    a.qe = q_exps;
+    a.ke = k_exps;
+    a.ve = v_exps;
+    a.o = o;
+    a.lse = lse;
+    a.BH = BH;
+    a.N = N;
+    a.causal = causal != 0;
+    a.scale = scale;
+    a.stream = static_cast<hipStream_t>(stream);
+    const hipError_t err = attn_fp8_launch(a);
     if (err != hipSuccess) {
         g_last_hip_error = static_cast<int>(err);
         return ATTN_HIP;

@@ -1,0 +1,522 @@
+// attn_fp8_kernel.hip -- FP8 attention forward for gfx950: block quantization
+// with incoherent processing, then the fused attention on FP8 operands.
+//
+// The FP8 mode of FlashAttention-3 as the pages outline it: both products on
+// FP8 matrix cores, one scale per block of the inputs instead of one per
+// tensor, and Q and K multiplied by a random orthogonal matrix before they are
+// quantized so that outliers spread over the head dimension ("FlashAttention
+// evolution", letsgetai.github.io, FlashAttention-3 section; "FlashAttention
+// 1-4 evolution cheat sheet", argus-lessons, FlashAttention-3 section).
+//
+// Formats (head dim 128):
+//   * FP8 is OCP E4M3, round to nearest even.
+//   * A quantization block is 64 rows of one head.  Its scale is 2^E with E
+//     the smallest integer such that the block's largest magnitude is at most
+//     448 * 2^E, stored as the E8M0 byte E + 127.  Power-of-two scales are
+//     what the gfx950 scaled MFMA applies itself
+//     (v_mfma_scale_f32_32x32x64_f8f6f4), so dequantization costs nothing.
+//   * Incoherent processing: x -> (x * s) H, random signs s, then the
+//     Sylvester Hadamard matrix H by its fast transform in fp32 (butterfly
+//     stages of stride 1, 2, ..., 64, each (a, b) -> (a + b, a - b)).  The
+//     product of rotated Q and K is d times the original: the caller divides
+//     the softmax scale by d.
+//   * Q and K: [BH][Np][128] bytes, Np = N rounded up to 64, rows past N zero.
+//     V: transposed, [BH][128][Np], and within every 64-key tile the keys are
+//     stored in the order the P operand of the P V product holds them: key r
+//     at position 32 ((r >> 2) & 1) + 16 (r >> 5) + 4 ((r >> 3) & 3) + (r & 3).
+//   * Exponents: one E8M0 byte per block, [BH][Np / 64].
+//
+// The attention kernel is the bf16 forward's design at FP8 rates: a
+// workgroup of 8 waves owns 256 queries (32 per wave) and walks 64-key tiles,
+// double-buffered in LDS through buffer_load ... lds; per tile each wave
+// computes S^T = K Q^T (two 32-key blocks, two K = 64 MFMAs each), the
+// softmax against a lagging reference max, and O^T += V^T P^T (four MFMAs
+// over the tile's 64 keys).  The softmax of tile t runs while the matrix
+// cores compute S of tile t+1 and P V of tile t-1.  P is rounded to E4M3
+// for the product (the reference may lag the row max by at most 8 in log2
+// units, so P <= 256 stays inside E4M3); O is divided by the fp32 sum of the
+// unrounded P, which also gives the LSE.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "attn_common.h"
+#include "attn_launch.h"
+
+namespace attn_gfx950 {
+namespace fp8 {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kD = 128;
+constexpr int kRowsBlk = 64;                 // quantization block = K/V tile rows
+constexpr int kWaves = 8;
+constexpr int kThreads = kWave * kWaves;
+constexpr int kBr = 32 * kWaves;             // queries per workgroup
+constexpr int kTileBytes = kRowsBlk * kD;    // one K tile or one V^T tile: 8 KB
+constexpr float kRefSlack = 8.f;             // P <= 2^8 inside E4M3's 448
+constexpr int kE8M0One = 127;
+
+// ---------------------------------------------------------------------------
+// Quantization
+
+// Smallest E with amax <= 448 * 2^E, from the bits of amax = (1 + f) 2^e:
+// E = e - 8 when 1 + f <= 1.75, else e - 7; 0 for amax == 0; E8M0 range.
+__device__ __forceinline__ int block_exp(float amax)
+{
+    if (!(amax > 0.f))
+        return 0;
+    const uint32_t u = __float_as_uint(amax);
+    const int e = (int)((u >> 23) & 0xffu) - 127;
+    const int E = (u & 0x7fffffu) <= 0x600000u ? e - 8 : e - 7;
+    return max(-127, min(127, E));
+}
+
+// One 64-row block of one head per workgroup (256 threads): thread t owns
+// columns 8 (t % 16) .. +7 of rows 16 p + t / 16, p = 0..3.  ROTATE applies
+// the signs and the fast Hadamard transform (three stages inside a thread,
+// four across the 16 threads of a row); TRANSPOSE writes V^T in the tile's
+// key order through LDS.
+template <bool ROTATE, bool TRANSPOSE>
+__global__ __launch_bounds__(256) void quantize_kernel(const __bf16 *__restrict__ x, uint8_t *__restrict__ out,
+                                                       uint8_t *__restrict__ exps, int N, int Np, int nblk,
+                                                       uint32_t s0, uint32_t s1, uint32_t s2, uint32_t s3)
+{
+    __shared__ float wmax[4];
+    __shared__ __attribute__((aligned(16))) uint8_t tr[TRANSPOSE ? kD * kRowsBlk : 16];
+    const int bh = blockIdx.x / nblk, blk = blockIdx.x % nblk;
+    const int t = threadIdx.x, c16 = t & 15, rsub = t >> 4;
+    float v[4][8];
+    float amax = 0.f;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int row = blk * kRowsBlk + 16 * p + rsub;
+        bf16x8 in = bf16x8{};
+        if (row < N)
+            in = *reinterpret_cast<const bf16x8 *>(x + ((size_t)bh * N + row) * kD + 8 * c16);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            v[p][e] = (float)in[e];
+        if constexpr (ROTATE) {
+            const uint32_t sw = (c16 < 4) ? s0 : (c16 < 8) ? s1 : (c16 < 12) ? s2 : s3;
+            const uint32_t bits = sw >> (8 * (c16 & 3));  // columns 8 c16 .. +7
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if ((bits >> e) & 1u)
+                    v[p][e] = -v[p][e];
+#pragma unroll
+            for (int h = 1; h < 8; h *= 2)
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    if ((i & h) == 0) {
+                        const float a = v[p][i], b = v[p][i + h];
+                        v[p][i] = a + b;
+                        v[p][i + h] = a - b;
+                    }
+#pragma unroll
+            for (int m = 1; m < 16; m *= 2)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float o = __shfl_xor(v[p][e], m, 16);
+                    v[p][e] = (c16 & m) ? o - v[p][e] : v[p][e] + o;
+                }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            amax = fmaxf(amax, fabsf(v[p][e]));
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m *= 2)
+        amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+    if ((t & 63) == 0)
+        wmax[t >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    const int E = block_exp(amax);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        uint32_t w[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            int u = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(v[p][4 * h + 0], -E),
+                                                    __builtin_amdgcn_ldexpf(v[p][4 * h + 1], -E), 0, false);
+            u = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(v[p][4 * h + 2], -E),
+                                                __builtin_amdgcn_ldexpf(v[p][4 * h + 3], -E), u, true);
+            w[h] = (uint32_t)u;
+        }
+        const int r = 16 * p + rsub;  // row in the block
+        if constexpr (!TRANSPOSE) {
+            *reinterpret_cast<u32x2 *>(out + ((size_t)bh * Np + blk * kRowsBlk + r) * kD + 8 * c16) = u32x2{w[0], w[1]};
+        } else {
+            const int pos = 32 * ((r >> 2) & 1) + 16 * (r >> 5) + 4 * ((r >> 3) & 3) + (r & 3);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                tr[(8 * c16 + e) * kRowsBlk + pos] = (uint8_t)(w[e >> 2] >> (8 * (e & 3)));
+        }
+    }
+    if constexpr (TRANSPOSE) {
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int chunk = t + 256 * i, row = chunk >> 2, part = chunk & 3;
+            *reinterpret_cast<u32x4 *>(out + ((size_t)bh * kD + row) * Np + blk * kRowsBlk + 16 * part) =
+                *reinterpret_cast<const u32x4 *>(tr + row * kRowsBlk + 16 * part);
+        }
+    }
+    if (t == 0)
+        exps[(size_t)bh * nblk + blk] = (uint8_t)(E + kE8M0One);
+}
+
+// ---------------------------------------------------------------------------
+// Attention
+
+// LDS swizzles (16-byte chunk c of row r at chunk position c ^ swz(r)).
+//  K rows are 128 bytes, two per 256-byte bank line; a ds_read_b128 by lanes
+//  0..15 reads rows 0..15 at one chunk: distinct positions need
+//  (r & 1, c ^ swz(r)) distinct, which (r & 7) ^ ((r >> 3) & 1) gives.
+//  V^T rows are 64 bytes, four per bank line: (r & 3, c ^ swz(r)) distinct
+//  over 16 rows needs swz(r) = (r >> 2) & 3.
+__device__ __forceinline__ int swz_k(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz_v(int r) { return (r >> 2) & 3; }
+
+struct F8Args {
+    const uint8_t *Q, *K, *VT;       // [BH][Np][128], [BH][Np][128], [BH][128][Np]
+    const uint8_t *qe, *ke, *ve;     // [BH][Np / 64] E8M0
+    __bf16 *O;                        // [BH][N][128]
+    float *LSE;                       // [BH][N] or null
+    int BH, N, Np, nblk, n_wg, nqt;
+    float c_log2;
+};
+
+__device__ __forceinline__ f32x16 mfma8(const i32x8 &a, const i32x8 &b, const f32x16 &c, int sa, int sb)
+{
+    // cbsz = blgp = 0: both operands E4M3; the E8M0 scales multiply A and B.
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
+__device__ __forceinline__ i32x8 lds_pair(const char *p0, const char *p1)
+{
+    const i32x4 lo = *LDS_PTR(const i32x4, p0);
+    const i32x4 hi = *LDS_PTR(const i32x4, p1);
+    return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_fp8_kernel(
+    const F8Args a)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    __shared__ __attribute__((aligned(1024))) char sk0[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sk1[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sv0[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char sv1[kTileBytes];
+
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int wave_u = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int n = lane & 31, half = lane >> 5;
+    const int N = a.N, Np = a.Np, nqt = a.nqt;
+    const float c_log2 = a.c_log2;
+
+    const int n_units = CAUSAL ? (nqt + 1) / 2 : nqt;
+    int bh, unit;
+    unit_of(blockIdx.x, a.n_wg, n_units, bh, unit);
+    const int npass = (CAUSAL && nqt - 1 - unit != unit) ? 2 : 1;
+
+    // Per-lane offsets.  DMA: wave w copies 1 KB slice w of each tile: K rows
+    // 8 w + lane / 8 (chunk lane % 8), V^T rows 16 w + lane / 4 (chunk lane % 4).
+    const int kr = 8 * wave_u + lane / 8, kp = lane % 8;
+    const uint32_t kdma = (uint32_t)(kr * kD + ((kp ^ swz_k(kr)) << 4));
+    const int vr = 16 * wave_u + lane / 4, vp = lane % 4;
+    const uint32_t vdma = (uint32_t)(vr * Np + ((vp ^ swz_v(vr)) << 4));
+    // S operand: row n of a 32-key block, bytes 64 st + 32 half .. +31 (chunks
+    // 4 st + 2 half + c).  P V operand: V^T row n of a 32-row block, bytes
+    // 32 half .. +31 of the tile (chunks 2 half + c).
+    uint32_t koff[2][2], voff[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+            koff[st][c] = (uint32_t)(n * kD + (((4 * st + 2 * half + c) ^ swz_k(n)) << 4));
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+        voff[c] = (uint32_t)(n * kRowsBlk + (((2 * half + c) ^ swz_v(n)) << 4));
+
+    const uint8_t *Kh = a.K + (size_t)bh * Np * kD;
+    const uint8_t *Vh = a.VT + (size_t)bh * kD * Np;
+    const uint8_t *keh = a.ke + (size_t)bh * a.nblk, *veh = a.ve + (size_t)bh * a.nblk;
+    const __amdgpu_buffer_rsrc_t vrsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void *)Vh, (short)0, (int)((uint32_t)kD * (uint32_t)Np), kBufferFlags);
+
+    for (int pass = 0; pass < npass; ++pass) {
+        const int qt = CAUSAL ? (pass == 0 ? nqt - 1 - unit : unit) : unit;
+        if (pass > 0)
+            __syncthreads();
+        const int q0 = qt * kBr;
+        const int qw0 = q0 + 32 * wave_u;
+        const int qidx = qw0 + n;
+        const bool q_ok = qidx < N;
+        const int kv_end = CAUSAL ? min(N, q0 + kBr) : N;
+        const int t_end = (kv_end + kRowsBlk - 1) / kRowsBlk;
+        const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)Kh, (short)0, (int)((uint32_t)kv_end * (uint32_t)kD), kBufferFlags);
+
+        auto load_k = [&](int t, char *buf) __attribute__((always_inline)) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, LDS_PTR(void, buf + wave_u * 1024), 16, kdma,
+                                                     (int)((uint32_t)t * (uint32_t)kTileBytes), 0, 0);
+        };
+        auto load_v = [&](int t, char *buf) __attribute__((always_inline)) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, LDS_PTR(void, buf + wave_u * 1024), 16, vdma,
+                                                     (int)((uint32_t)t * (uint32_t)kRowsBlk), 0, 0);
+        };
+
+        load_k(0, sk0);
+        load_k(1, sk1);  // past kv_end: zeros, no memory access
+        // V buffer 1 is multiplied by the zero P of "tile -1" in the first step:
+        // it must hold finite values.
+#pragma unroll
+        for (int i = 0; i < kTileBytes / (16 * kThreads); ++i)
+            *LDS_PTR(u32x4, sv1 + 16 * (tid + i * kThreads)) = u32x4{};
+
+        // Q^T operand (E4M3 bytes 64 st + 32 half .. +31 of this lane's query
+        // row) and its block exponent, shared by the wave (32 queries of one
+        // 64-row block).
+        i32x8 qop[2];
+        {
+            const uint8_t *qrow = a.Q + ((size_t)bh * Np + (q_ok ? qidx : 0)) * kD + 32 * half;
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                const i32x4 lo = *reinterpret_cast<const i32x4 *>(qrow + 64 * st);
+                const i32x4 hi = *reinterpret_cast<const i32x4 *>(qrow + 64 * st + 16);
+                qop[st] = q_ok ? i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]} : i32x8{};
+            }
+        }
+        const int qs = qw0 < N ? (int)a.qe[(size_t)bh * a.nblk + qw0 / kRowsBlk] : kE8M0One;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+
+        // Scores of the 64-key tile t (two 32-key blocks) from K buffer kb.
+        auto scores = [&](const char *kbuf, int ks, f32x16 *s) __attribute__((always_inline)) {
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                s[b] = f32x16{};
+#pragma unroll
+                for (int st = 0; st < 2; ++st)
+                    s[b] = mfma8(lds_pair(kbuf + b * 32 * kD + koff[st][0], kbuf + b * 32 * kD + koff[st][1]),
+                                 qop[st], s[b], ks, qs);
+            }
+        };
+        f32x16 sc[2];
+        scores(sk0, (int)keh[0], sc);
+
+        // Register 4 j + e of block b holds key 64 t + 32 b + 8 j + 4 half + e.
+        auto visible = [&](int t, int b, int r) __attribute__((always_inline)) {
+            const int key = 64 * t + 32 * b + 8 * (r >> 2) + 4 * half + (r & 3);
+            return key < N && (!CAUSAL || key <= qidx);
+        };
+        auto tile_masked = [&](int t) __attribute__((always_inline)) {
+            return 64 * t + 63 >= N || (CAUSAL && 64 * t + 63 > qw0);
+        };
+        float m_ref, m_sub, m_thr;
+        auto set_ref = [&](float m) __attribute__((always_inline)) {
+            m_ref = m;
+            m_sub = (m == kNegInf) ? 0.f : m;
+            m_thr = m + kRefSlack;
+        };
+        {
+            float mx = kNegInf;
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    mx = fmaxf(mx, visible(0, b, r) ? sc[b][r] * c_log2 : kNegInf);
+            set_ref(wave_half_max(mx));
+        }
+        f32x16 oacc[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            oacc[b] = f32x16{};
+        float l_run = 0.f;
+        bool pending = false;
+        float alpha_pend = 1.f;
+        i32x8 pb_prev = i32x8{};
+        int vs_prev = kE8M0One;
+
+        for (int t = 0; t < t_end; ++t) {
+            char *kcur = (t & 1) ? sk1 : sk0;   // K tile t (already consumed into sc)
+            char *knext = (t & 1) ? sk0 : sk1;  // K tile t+1
+            char *vprev = (t & 1) ? sv0 : sv1;  // V tile t-1
+            char *vcur = (t & 1) ? sv1 : sv0;   // V tile t, loaded now
+            // Tile t+1's K and tile t-1's V have landed, and every wave is done
+            // with K tile t and V tile t-2, whose buffers are refilled now.
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            load_k(t + 2, kcur);  // past kv_end: zeros, no memory access
+            load_v(t, vcur);
+
+            // P of tile t against the reference, rounded to E4M3 in the order
+            // of the P V operand: byte 4 w + i is register 4 (w & 3) + i of
+            // block w >> 2.
+            const bool masked = tile_masked(t);
+            float p[2][16];
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    p[b][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[b][r], c_log2, -m_sub));
+                    if (masked && !visible(t, b, r))
+                        p[b][r] = 0.f;
+                }
+            float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                rs0 += p[0][r];
+                rs1 += p[1][r];
+            }
+            l_run += rs0 + rs1;
+            i32x8 pb;
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+                const float *pp = &p[w >> 2][4 * (w & 3)];
+                int u = __builtin_amdgcn_cvt_pk_fp8_f32(pp[0], pp[1], 0, false);
+                pb[w] = __builtin_amdgcn_cvt_pk_fp8_f32(pp[2], pp[3], u, true);
+            }
+
+            // Scores of tile t+1 (past the end: zero rows, discarded) and P V
+            // of tile t-1.
+            f32x16 sn[2];
+            const int ks_next = (t + 1 < t_end) ? (int)keh[t + 1] : kE8M0One;
+            scores(knext, ks_next, sn);
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+                oacc[db] = mfma8(lds_pair(vprev + db * 32 * kRowsBlk + voff[0], vprev + db * 32 * kRowsBlk + voff[1]),
+                                 pb_prev, oacc[db], vs_prev, kE8M0One);
+
+            float mx = kNegInf;
+            if (t + 1 < t_end) {
+                const bool nmasked = tile_masked(t + 1);
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        mx = fmaxf(mx, (!nmasked || visible(t + 1, b, r)) ? sn[b][r] * c_log2 : kNegInf);
+            }
+            const bool reref = __builtin_amdgcn_ballot_w64(mx > m_thr) != 0;
+
+            // The step's region: 8 MFMAs, each followed by a share of the
+            // softmax VALU work and the operand reads for the MFMAs after it.
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x402, 18, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            asm volatile("" : "+v"(pb), "+v"(l_run));
+
+            if (pending) {
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    oacc[b] *= alpha_pend;
+            }
+            pending = reref;
+            if (reref) {
+                const float m_new = fmaxf(m_ref, wave_half_max(mx));
+                alpha_pend = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+                l_run *= alpha_pend;
+                set_ref(m_new);
+            }
+            sc[0] = sn[0];
+            sc[1] = sn[1];
+            pb_prev = pb;
+            vs_prev = (int)veh[t];
+        }
+        // P V of the last tile.
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        {
+            char *vlast = ((t_end - 1) & 1) ? sv1 : sv0;
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+                oacc[db] = mfma8(lds_pair(vlast + db * 32 * kRowsBlk + voff[0], vlast + db * 32 * kRowsBlk + voff[1]),
+                                 pb_prev, oacc[db], vs_prev, kE8M0One);
+            if (pending) {
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    oacc[b] *= alpha_pend;
+            }
+        }
+
+        const float l_tot = wave_half_sum(l_run);
+        if (q_ok) {
+            const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+            __bf16 *orow = a.O + ((size_t)bh * N + qidx) * kD;
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    u32x2 w;
+                    w[0] = pack_bf16x2(oacc[b][4 * j + 0] * inv, oacc[b][4 * j + 1] * inv);
+                    w[1] = pack_bf16x2(oacc[b][4 * j + 2] * inv, oacc[b][4 * j + 3] * inv);
+                    *reinterpret_cast<u32x2 *>(orow + 32 * b + 8 * j + 4 * half) = w;
+                }
+            if (a.LSE != nullptr && half == 0)
+                a.LSE[(size_t)bh * N + qidx] = (m_ref + __builtin_log2f(l_tot)) * 0.69314718055994530942f;
+        }
+    }
+#endif
+}
+
+}  // namespace fp8
+}  // namespace attn_gfx950
+
+int64_t attn_fp8_rows(int64_t N) { return (N + 63) / 64 * 64; }
+
+hipError_t attn_fp8_quantize_launch(const AttnFp8Quantize &q)
+{
+    using namespace attn_gfx950::fp8;
+    const int Np = (int)attn_fp8_rows(q.N), nblk = Np / kRowsBlk;
+    const int grid = (int)(q.BH * nblk);
+    const uint32_t *s = q.sign_bits;
+    const uint32_t s0 = s ? s[0] : 0, s1 = s ? s[1] : 0, s2 = s ? s[2] : 0, s3 = s ? s[3] : 0;
+    const __bf16 *x = (const __bf16 *)q.x;
+    uint8_t *out = (uint8_t *)q.out, *exps = (uint8_t *)q.exps;
+    if (q.transpose)
+        hipLaunchKernelGGL((quantize_kernel<false, true>), dim3(grid), dim3(256), 0, q.stream, x, out, exps, (int)q.N, Np,
+                           nblk, 0u, 0u, 0u, 0u);
+    else if (s)
+        hipLaunchKernelGGL((quantize_kernel<true, false>), dim3(grid), dim3(256), 0, q.stream, x, out, exps, (int)q.N, Np,
+                           nblk, s0, s1, s2, s3);
+    else
+        hipLaunchKernelGGL((quantize_kernel<false, false>), dim3(grid), dim3(256), 0, q.stream, x, out, exps, (int)q.N, Np,
+                           nblk, 0u, 0u, 0u, 0u);
+    return hipGetLastError();
+}
+
+hipError_t attn_fp8_launch(const AttnFp8Launch &l)
+{
+    using namespace attn_gfx950::fp8;
+    F8Args a;
+    a.Q = (const uint8_t *)l.q8;
+    a.K = (const uint8_t *)l.k8;
+    a.VT = (const uint8_t *)l.vt8;
+    a.qe = (const uint8_t *)l.qe;
+    a.ke = (const uint8_t *)l.ke;
+    a.ve = (const uint8_t *)l.ve;
+    a.O = (__bf16 *)l.o;
+    a.LSE = l.lse;
+    a.BH = (int)l.BH;
+    a.N = (int)l.N;
+    a.Np = (int)attn_fp8_rows(l.N);
+    a.nblk = a.Np / kRowsBlk;
+    a.nqt = (int)((l.N + kBr - 1) / kBr);
+    a.n_wg = (int)(l.BH * (l.causal ? (a.nqt + 1) / 2 : a.nqt));
+    a.c_log2 = l.scale * attn_gfx950::kLog2e;
+    if (l.causal)
+        hipLaunchKernelGGL((attn_fwd_fp8_kernel<true>), dim3(a.n_wg), dim3(kThreads), 0, l.stream, a);
+    else
+        hipLaunchKernelGGL((attn_fwd_fp8_kernel<false>), dim3(a.n_wg), dim3(kThreads), 0, l.stream, a);
+    return hipGetLastError();
+}

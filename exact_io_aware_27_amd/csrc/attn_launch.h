@@ -53,3 +53,29 @@ int64_t attn_bwd_workgroups(int64_t BH, int64_t N);
 
 // Enqueue the two backward kernels; returns hipGetLastError() after them.
 hipError_t attn_bwd_launch(const AttnBwdLaunch &a);
+
+// FP8 path (head dim 128).  Padded rows per head: N rounded up to 64.
+int64_t attn_fp8_rows(int64_t N);
+
+// One validated attn_fp8_quantize call.
+struct AttnFp8Quantize {
+    const void *x;               // [BH][N][128] bf16
+    void *out, *exps;            // FP8 bytes and E8M0 block exponents
+    const uint32_t *sign_bits;   // host, 4 words, or null (no rotation)
+    bool transpose;              // V^T layout (no rotation)
+    int64_t BH, N;
+    hipStream_t stream;
+};
+hipError_t attn_fp8_quantize_launch(const AttnFp8Quantize &q);
+
+// One validated attn_fwd_fp8 call.
+struct AttnFp8Launch {
+    const void *q8, *k8, *vt8, *qe, *ke, *ve;
+    void *o;
+    float *lse;
+    int64_t BH, N;
+    bool causal;
+    float scale;
+    hipStream_t stream;
+};
+hipError_t attn_fp8_launch(const AttnFp8Launch &a);

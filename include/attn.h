@@ -57,9 +57,10 @@ enum attn_status {
     ATTN_MISALIGNED = 5,    /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
     ATTN_ALIAS = 6,         /* o or lse overlaps q, k or v, or o overlaps lse */
     ATTN_HIP = 7,           /* the kernel launch failed; see attn_last_hip_error() */
-    ATTN_BAD_WORKSPACE = 8  /* attn_fwd_splitkv, attn_bwd: workspace NULL, not 16-byte
+    ATTN_BAD_WORKSPACE = 8, /* attn_fwd_splitkv, attn_bwd: workspace NULL, not 16-byte
                                aligned, smaller than the *_workspace_bytes() size, or
                                overlapping a tensor of the call */
+    ATTN_BAD_ARGUMENT = 9   /* attn_fp8_quantize: signs given with the transposed layout */
 };
 
 /*
@@ -176,6 +177,56 @@ ATTN_API int attn_bwd(const void *q, const void *k, const void *v, const void *o
 /* Bytes of workspace attn_bwd needs (8 B H N); -1 if the arguments are
  * invalid (negative, d not 64/128, or the size overflows). */
 ATTN_API int64_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d);
+
+/*
+ * FP8 forward (head dim 128): block quantization with incoherent processing,
+ * then attention on the FP8 operands -- the FP8 mode of FlashAttention-3
+ * ("FlashAttention evolution", letsgetai.github.io, FlashAttention-3 section
+ * and results; "FlashAttention 1-4 evolution cheat sheet", argus-lessons,
+ * FlashAttention-3 section).  An approximation of attn_fwd, not an exact
+ * result: inputs and P are rounded to FP8.
+ *
+ * Formats.  FP8 is OCP E4M3 (round to nearest even).  Rows are quantized in
+ * blocks of 64 consecutive rows of one head; a block's scale is 2^E, E the
+ * smallest integer with max|x| <= 448 * 2^E, stored as one E8M0 byte E + 127
+ * per block: [B][H][Np / 64], Np = attn_fp8_padded_rows(N) = N rounded up
+ * to 64.  Q and K are [B][H][Np][128] bytes, V is stored transposed as
+ * [B][H][128][Np] with the keys of every 64-key tile permuted (key r at
+ * position 32 ((r >> 2) & 1) + 16 (r >> 5) + 4 ((r >> 3) & 3) + (r & 3)),
+ * which is the order the kernel's P V product consumes them in.  Rows
+ * (keys) past N are zero.
+ */
+ATTN_API int64_t attn_fp8_padded_rows(int64_t N);
+
+/*
+ * attn_fp8_quantize -- bf16 x [B][H][N][128] (device, 16-byte aligned) to
+ * FP8: out gets [B][H][Np][128] bytes (transpose == 0) or the permuted
+ * [B][H][128][Np] V layout (transpose != 0); exps gets [B][H][Np / 64] E8M0
+ * bytes.  sign_bits: NULL, or a HOST array of 4 words whose bit c (word
+ * c / 32, bit c % 32) set makes column c's sign -1: then each row is first
+ * rotated, x -> (x * s) H with H the 128 x 128 Sylvester Hadamard matrix
+ * (+-1 entries, no 1/sqrt(128)), computed in fp32 by the fast transform with
+ * strides 1, 2, ..., 64.  Q and K rotated with the same signs keep their
+ * product times 128, so attn_fwd_fp8 then takes scale / 128.  Errors:
+ * BAD_SHAPE, UNSUPPORTED_D (d != 128), BAD_ARGUMENT (signs with transpose),
+ * (empty -> OK), NULL_PTR, MISALIGNED, ALIAS.  One kernel on `stream`.
+ */
+ATTN_API int attn_fp8_quantize(const void *x, int64_t B, int64_t H, int64_t N, int64_t d, int transpose,
+                      const uint32_t *sign_bits, void *out, void *exps, void *stream);
+
+/*
+ * attn_fwd_fp8 -- O (bf16 [B][H][N][128]) and LSE (fp32 [B][H][N] or NULL)
+ * of softmax(scale * Q K^T) V from the FP8 operands attn_fp8_quantize
+ * produced (q8, k8 rows; vt8 transposed; their exponent arrays).  Both
+ * products run on the FP8 matrix cores with the block scales applied by the
+ * hardware; P is rounded to E4M3 for the P V product and O is divided by the
+ * fp32 sum of the unrounded P.  causal, scale, stream as attn_fwd.  Errors as
+ * attn_fwd (d != 128 is UNSUPPORTED_D); one kernel on `stream`.
+ */
+ATTN_API int attn_fwd_fp8(const void *q8, const void *k8, const void *vt8, const void *q_exps,
+                 const void *k_exps, const void *v_exps, void *o, float *lse,
+                 int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+                 void *stream);
 
 /* Static, human-readable name of a status code ("ATTN_OK", ...). */
 ATTN_API const char *attn_status_string(int status);

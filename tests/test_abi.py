@@ -30,7 +30,8 @@ def _declared():
 
 def test_header_declares_the_abi():
     assert set(_declared()) == {"attn_fwd", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_bytes",
-                                "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_string",
+                                "attn_bwd", "attn_bwd_workspace_bytes", "attn_fp8_padded_rows",
+                                "attn_fp8_quantize", "attn_fwd_fp8", "attn_status_string",
                                 "attn_last_hip_error"}
 
 
@@ -45,7 +46,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_status_strings(lib):
     names = ["ATTN_OK", "ATTN_NULL_PTR", "ATTN_BAD_SHAPE", "ATTN_UNSUPPORTED_D",
-             "ATTN_BAD_SCALE", "ATTN_MISALIGNED", "ATTN_ALIAS", "ATTN_HIP", "ATTN_BAD_WORKSPACE"]
+             "ATTN_BAD_SCALE", "ATTN_MISALIGNED", "ATTN_ALIAS", "ATTN_HIP", "ATTN_BAD_WORKSPACE",
+             "ATTN_BAD_ARGUMENT"]
     for code, name in enumerate(names):
         assert lib.attn_status_string(code).decode() == name
     assert lib.attn_status_string(99).decode() == "ATTN_UNKNOWN_STATUS"
@@ -164,6 +166,34 @@ def test_bwd_workspace_bytes(lib):
     assert f(1, 1, 0, 64) == 0
     for bad in [(-1, 3, 7, 128), (2, 3, -7, 128), (2, 3, 7, 96), (1 << 40, 1 << 20, 1 << 10, 128)]:
         assert f(*bad) == -1
+
+
+def _quant(lib, x=Q, B=2, H=3, N=100, d=128, tr=0, signs=None, out=O, ex=L):
+    return lib.attn_fp8_quantize(x, B, H, N, d, tr, signs, out, ex, None)
+
+
+def _fp8(lib, q=Q, k=K, v=V, qe=W, ke=W + 4096, ve=W + 8192, o=O, lse=L, B=2, H=3, N=100, d=128, causal=1,
+         scale=0.1):
+    return lib.attn_fwd_fp8(q, k, v, qe, ke, ve, o, lse, B, H, N, d, causal, scale, None)
+
+
+def test_fp8_argument_errors_before_any_hip_call(lib):
+    import ctypes
+    bits = ctypes.cast((ctypes.c_uint32 * 4)(1, 2, 3, 4), ctypes.c_void_p)
+    assert lib.attn_fp8_padded_rows(100) == 128 and lib.attn_fp8_padded_rows(64) == 64
+    assert lib.attn_fp8_padded_rows(0) == 0 and lib.attn_fp8_padded_rows(-1) == -1
+    assert _quant(lib, B=-1) == 2 and _quant(lib, N=1 << 24) == 2
+    assert _quant(lib, d=64) == 3
+    assert _quant(lib, tr=1, signs=bits) == 9
+    assert _quant(lib, N=0, x=None) == 0
+    assert _quant(lib, x=None) == 1 and _quant(lib, ex=None) == 1
+    assert _quant(lib, x=Q + 8) == 5 and _quant(lib, out=O + 4) == 5
+    assert _quant(lib, out=Q + 64) == 6 and _quant(lib, ex=Q) == 6
+    assert _fp8(lib, N=-1) == 2 and _fp8(lib, d=64) == 3 and _fp8(lib, scale=float("nan")) == 4
+    assert _fp8(lib, B=0, q=None) == 0
+    assert _fp8(lib, q=None) == 1 and _fp8(lib, ve=None) == 1 and _fp8(lib, o=None) == 1
+    assert _fp8(lib, k=K + 8) == 5 and _fp8(lib, lse=L + 1) == 5
+    assert _fp8(lib, o=Q) == 6 and _fp8(lib, lse=W) == 6 and _fp8(lib, lse=O) == 6
 
 
 def test_binding_rejects_mismatched_tensors():

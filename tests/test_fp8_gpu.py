@@ -1,0 +1,165 @@
+"""FP8 forward path (attn_fp8_quantize, attn_fwd_fp8) against the FP8
+oracle (oracle/fp8_oracle.py), on a GPU.
+
+  * Quantization is byte work: the codes and exponents must equal the
+    oracle's bit for bit (the rotation's fp32 roundings are taken in the same
+    order on both sides).
+  * The attention is compared with exact attention of the dequantized
+    operands.  What remains is P's rounding to E4M3 before P V, whose size the
+    oracle predicts per element (sigma, from the actual P and V), plus one
+    bf16 rounding of O: the mean of (dO / sigma_total)^2 must stay near 1 and
+    no element may pass 6 sigma_total.  LSE comes from the unrounded P:
+    |dLSE| <= 1e-3 as for attn_fwd.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import fp8_oracle as f8
+from exact_io_aware_27_amd import inputs
+import parity
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def codes_of(t):
+    """uint8 E4M3 bytes -> float64 values."""
+    return t.cpu().view(torch.float8_e4m3fn).double().numpy()
+
+
+def key_position(r):
+    return 32 * ((r >> 2) & 1) + 16 * (r >> 5) + 4 * ((r >> 3) & 3) + (r & 3)
+
+
+def untranspose(vt, N):
+    """[B, H, 128, Np] permuted V^T codes -> [B, H, Np, 128] in key order."""
+    B, H, d, Np = vt.shape
+    r = np.arange(Np)
+    pos = (r // 64) * 64 + key_position(r % 64)
+    return np.swapaxes(vt[..., pos], -1, -2)
+
+
+@pytest.mark.parametrize("B,H,N,rotate", [(1, 2, 200, False), (1, 2, 200, True), (2, 1, 1, True),
+                                          (1, 1, 64, False), (1, 3, 333, True), (1, 1, 1000, False)])
+def test_quantize_is_bit_exact(B, H, N, rotate):
+    from exact_io_aware_27_amd import attn
+    q, _, v = inputs.make_qkv_outliers(B, H, N, 128, seed=4000 + N, frac=1e-2)
+    signs = inputs.make_signs(128, seed=4001).numpy() if rotate else None
+    say("case: quantize", (B, H, N), "rotated" if rotate else "plain")
+    qd, vd = q.to(DEV), v.to(DEV)
+    q8, qe = attn.fp8_quantize(qd, signs=signs)
+    vt8, ve = attn.fp8_quantize(vd, transpose=True)
+    torch.cuda.synchronize()
+    ref = f8.prepare_fp8(q, q, v, signs=signs)
+    Np = attn.fp8_padded_rows(N)
+    want_q = np.zeros((B, H, Np, 128))
+    want_q[:, :, :N] = ref["qc"]
+    want_v = np.zeros((B, H, Np, 128))
+    want_v[:, :, :N] = ref["vc"]
+    np.testing.assert_array_equal(codes_of(q8), want_q)
+    np.testing.assert_array_equal(qe.cpu().numpy().astype(np.int64) - 127, ref["qe"])
+    np.testing.assert_array_equal(untranspose(codes_of(vt8), N), want_v)
+    np.testing.assert_array_equal(ve.cpu().numpy().astype(np.int64) - 127, ref["ve"])
+
+
+def check_attention(B, H, N, causal, rotate, seed, outliers=False, what=""):
+    from exact_io_aware_27_amd import attn
+    d = 128
+    if outliers:
+        q, k, v = inputs.make_qkv_outliers(B, H, N, d, seed=seed, frac=1e-2)
+    else:
+        q, k, v = inputs.make_qkv(B, H, N, d, seed=seed)
+    signs = inputs.make_signs(d, seed=seed + 1).numpy() if rotate else None
+    scale = 1.0 / math.sqrt(d)
+    say("case:", what, (B, H, N), "causal" if causal else "non-causal", "rotated" if rotate else "plain")
+    o, lse = attn.attention_fp8(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, scale=scale, signs=signs)
+    torch.cuda.synchronize()
+    prep = f8.prepare_fp8(q, k, v, signs=signs)
+    o_ref, lse_ref, sigma = f8.attention_fp64(prep["q"], prep["k"], prep["v"], causal,
+                                              scale / prep["qk_factor"], p_rounding=True)
+    og = o.double().cpu().numpy()
+    rounding = parity.bf16_half_ulp(np.maximum(np.abs(o_ref), np.abs(og)))
+    total = np.sqrt(sigma ** 2 + rounding ** 2 / 3 + (1e-5) ** 2)
+    z = (og - o_ref) / total
+    dl = np.abs(lse.double().cpu().numpy() - lse_ref)
+    rep = dict(mean_z2=float(np.mean(z ** 2)), max_z=float(np.abs(z).max()), max_abs=float(np.abs(og - o_ref).max()),
+               lse=float(dl.max()), finite=bool(np.isfinite(og).all()))
+    say("  ", rep)
+    assert rep["finite"]
+    assert rep["mean_z2"] <= 2.0, rep
+    assert rep["max_z"] <= 6.0, rep
+    assert rep["lse"] <= 1e-3, rep
+    return o, q, k, v, prep
+
+
+@pytest.mark.parametrize("N,causal,rotate", [(256, False, False), (256, True, True), (100, True, False),
+                                             (1, True, True), (1000, False, True), (700, True, True),
+                                             (513, True, False)])
+def test_attention_matches_oracle(N, causal, rotate):
+    check_attention(1, 2, N, causal, rotate, seed=4100 + N + causal, what="fp8")
+
+
+def test_many_heads_with_outliers():
+    check_attention(2, 3, 300, True, True, seed=4200, outliers=True, what="outliers")
+
+
+def test_incoherent_processing_lowers_the_error_on_the_gpu():
+    """The GPU path's error against exact bf16-input attention, with and
+    without the rotation, on outlier-heavy input (the oracle's error study,
+    run through the kernels)."""
+    from exact_io_aware_27_amd import attn
+    B, H, N, d = 1, 4, 512, 128
+    q, k, v = inputs.make_qkv_outliers(B, H, N, d, seed=4300, frac=1e-2)
+    scale = 1.0 / math.sqrt(d)
+    exact, _ = oracle.attention(q, k, v, False, scale)
+    errs = {}
+    for rotate in (False, True):
+        signs = inputs.make_signs(d, seed=4301).numpy() if rotate else None
+        o, _ = attn.attention_fp8(q.to(DEV), k.to(DEV), v.to(DEV), causal=False, scale=scale, signs=signs)
+        torch.cuda.synchronize()
+        errs[rotate] = float(np.sqrt(np.mean((o.double().cpu().numpy() - exact) ** 2)))
+    say("   RMSE vs exact: plain %.4g, rotated %.4g (ratio %.2f)" % (errs[False], errs[True], errs[False] / errs[True]))
+    assert errs[False] / errs[True] > 1.5
+
+
+def test_long_causal_shape_sampled_rows():
+    """B=2 H=32 N=8192 causal: a sample of query rows of two heads against
+    the oracle (exact attention of the dequantized operands, row by row)."""
+    from exact_io_aware_27_amd import attn
+    w = [x for x in inputs.WORKLOADS if x.name == "long_causal"][0]
+    q, k, v = inputs.workload_qkv(w)
+    signs = inputs.make_signs(w.d, seed=w.seed + 1).numpy()
+    say("case: long_causal fp8", (w.B, w.H, w.N, w.d))
+    o, lse = attn.attention_fp8(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, scale=w.scale, signs=signs)
+    torch.cuda.synchronize()
+    for b, h in ((0, 3), (1, 30)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        prep = f8.prepare_fp8(q[sl], k[sl], v[sl], signs=signs)
+        rows = inputs.row_subset(w.N, 96, w.seed, b * w.H + h, (0, w.N - 1)).numpy()
+        o_ref, lse_ref, sigma = _causal_rows(prep, rows, w.scale)
+        og = o[b, h, rows].double().cpu().numpy()[None, None]
+        rounding = parity.bf16_half_ulp(np.maximum(np.abs(o_ref), np.abs(og)))
+        z = (og - o_ref) / np.sqrt(sigma ** 2 + rounding ** 2 / 3 + 1e-10)
+        dl = np.abs(lse[b, h, rows].double().cpu().numpy() - lse_ref[0, 0])
+        say("   head (%d, %d): mean z^2 %.3f, max |z| %.2f, max |dLSE| %.2e" % (b, h, np.mean(z ** 2), np.abs(z).max(), dl.max()))
+        assert np.mean(z ** 2) <= 2.0 and np.abs(z).max() <= 6.0 and dl.max() <= 1e-3
+
+
+def _causal_rows(prep, rows, scale):
+    """Oracle rows of a causal head: each sampled query against its visible
+    prefix of keys."""
+    outs = [f8.attention_fp64(prep["q"][:, :, [r]], prep["k"][:, :, :r + 1], prep["v"][:, :, :r + 1], False,
+                              scale / prep["qk_factor"], p_rounding=True) for r in rows]
+    return (np.concatenate([x[0] for x in outs], axis=2), np.concatenate([x[1] for x in outs], axis=2),
+            np.concatenate([x[2] for x in outs], axis=2))
