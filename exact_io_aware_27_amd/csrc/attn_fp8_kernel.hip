@@ -216,7 +216,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int wave_u = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int n = lane & 31, half = lane >> 5;
     const int N = a.N, Np = a.Np, nqt = a.nqt;
     const float c_log2 = a.c_log2;
 
@@ -224,25 +223,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     int bh, unit;
     unit_of(blockIdx.x, a.n_wg, n_units, bh, unit);
     const int npass = (CAUSAL && nqt - 1 - unit != unit) ? 2 : 1;
-
-    // Per-lane offsets.  DMA: wave w copies 1 KB slice w of each tile: K rows
-    // 8 w + lane / 8 (chunk lane % 8), V^T rows 16 w + lane / 4 (chunk lane % 4).
-    const int kr = 8 * wave_u + lane / 8, kp = lane % 8;
-    const uint32_t kdma = (uint32_t)(kr * kD + ((kp ^ swz_k(kr)) << 4));
-    const int vr = 16 * wave_u + lane / 4, vp = lane % 4;
-    const uint32_t vdma = (uint32_t)(vr * Np + ((vp ^ swz_v(vr)) << 4));
-    // S operand: row n of a 32-key block, bytes 64 st + 32 half .. +31 (chunks
-    // 4 st + 2 half + c).  P V operand: V^T row n of a 32-row block, bytes
-    // 32 half .. +31 of the tile (chunks 2 half + c).
-    uint32_t koff[2][2], voff[2];
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-            koff[st][c] = (uint32_t)(n * kD + (((4 * st + 2 * half + c) ^ swz_k(n)) << 4));
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-        voff[c] = (uint32_t)(n * kRowsBlk + (((2 * half + c) ^ swz_v(n)) << 4));
 
     const uint8_t *Kh = a.K + (size_t)bh * Np * kD;
     const uint8_t *Vh = a.VT + (size_t)bh * kD * Np;
@@ -254,6 +234,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int qt = CAUSAL ? (pass == 0 ? nqt - 1 - unit : unit) : unit;
         if (pass > 0)
             __syncthreads();
+        // Per-lane offsets, computed afresh in each pass from an opaque copy of
+        // the lane index so that they are not kept live across passes.  DMA:
+        // wave w copies 1 KB slice w of each tile: K rows 8 w + lane / 8
+        // (chunk lane % 8), V^T rows 16 w + lane / 4 (chunk lane % 4).
+        int lane_p = lane;
+        asm volatile("" : "+v"(lane_p));
+        const int n = lane_p & 31, half = lane_p >> 5;
+        const int kr = 8 * wave_u + lane_p / 8, kp = lane_p % 8;
+        const uint32_t kdma = (uint32_t)(kr * kD + ((kp ^ swz_k(kr)) << 4));
+        const int vr = 16 * wave_u + lane_p / 4, vp = lane_p % 4;
+        const uint32_t vdma = (uint32_t)(vr * Np + ((vp ^ swz_v(vr)) << 4));
+        // S operand: row n of a 32-key block, bytes 64 st + 32 half .. +31 (chunks
+        // 4 st + 2 half + c).  P V operand: V^T row n of a 32-row block, bytes
+        // 32 half .. +31 of the tile (chunks 2 half + c).
+        uint32_t koff[2][2], voff[2];
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+                koff[st][c] = (uint32_t)(n * kD + (((4 * st + 2 * half + c) ^ swz_k(n)) << 4));
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+            voff[c] = (uint32_t)(n * kRowsBlk + (((2 * half + c) ^ swz_v(n)) << 4));
         const int q0 = qt * kBr;
         const int qw0 = q0 + 32 * wave_u;
         const int qidx = qw0 + n;
@@ -294,6 +297,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             }
         }
         const int qs = qw0 < N ? (int)a.qe[(size_t)bh * a.nblk + qw0 / kRowsBlk] : kE8M0One;
+        const int ks0 = keh[0], ks1 = keh[min(1, a.nblk - 1)];
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
 
@@ -309,15 +313,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             }
         };
         f32x16 sc[2];
-        scores(sk0, (int)keh[0], sc);
+        scores(sk0, ks0, sc);
 
         // Register 4 j + e of block b holds key 64 t + 32 b + 8 j + 4 half + e.
         auto visible = [&](int t, int b, int r) __attribute__((always_inline)) {
             const int key = 64 * t + 32 * b + 8 * (r >> 2) + 4 * half + (r & 3);
             return key < N && (!CAUSAL || key <= qidx);
-        };
-        auto tile_masked = [&](int t) __attribute__((always_inline)) {
-            return 64 * t + 63 >= N || (CAUSAL && 64 * t + 63 > qw0);
         };
         float m_ref, m_sub, m_thr;
         auto set_ref = [&](float m) __attribute__((always_inline)) {
@@ -342,38 +343,55 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         bool pending = false;
         float alpha_pend = 1.f;
         i32x8 pb_prev = i32x8{};
-        int vs_prev = kE8M0One;
+        int ks = ks1, vs = kE8M0One;  // exponents of K tile 1 and of "V tile -1"
 
-        for (int t = 0; t < t_end; ++t) {
-            char *kcur = (t & 1) ? sk1 : sk0;   // K tile t (already consumed into sc)
-            char *knext = (t & 1) ? sk0 : sk1;  // K tile t+1
-            char *vprev = (t & 1) ? sv0 : sv1;  // V tile t-1
-            char *vcur = (t & 1) ? sv1 : sv0;   // V tile t, loaded now
+        // One 64-key step (tile t, K buffer P = t % 2).  MASKED: tile t needs
+        // the causal / sequence-end mask; NEXT_MASKED: tile t+1 does (past
+        // the last tile every key is invisible, so the last step takes it
+        // too).  ks: exponent of K tile t+1; vs: of V tile t-1.  Both were
+        // loaded in the previous step, so nothing in a step waits on memory
+        // but its opening barrier.
+        auto step = [&](int t, auto parity_tag, auto masked_tag, auto next_masked_tag) __attribute__((always_inline)) {
+            constexpr int P = decltype(parity_tag)::value;
+            constexpr bool MASKED = decltype(masked_tag)::value;
+            constexpr bool NEXT_MASKED = decltype(next_masked_tag)::value;
+            char *kcur = P ? sk1 : sk0;   // K tile t (already consumed into sc)
+            char *knext = P ? sk0 : sk1;  // K tile t+1
+            char *vprev = P ? sv0 : sv1;  // V tile t-1
+            char *vcur = P ? sv1 : sv0;   // V tile t, loaded now
             // Tile t+1's K and tile t-1's V have landed, and every wave is done
             // with K tile t and V tile t-2, whose buffers are refilled now.
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
             load_k(t + 2, kcur);  // past kv_end: zeros, no memory access
             load_v(t, vcur);
+            const int ks_pf = keh[min(t + 2, a.nblk - 1)], vs_pf = veh[t];
+            // Keep the LDS offsets opaque (so they ride in the ds_read offset
+            // field instead of being hoisted as per-buffer sums) and the
+            // softmax inside its step.
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+                asm volatile("" : "+v"(koff[st][0]), "+v"(koff[st][1]));
+            asm volatile("" : "+v"(voff[0]), "+v"(voff[1]));
+            asm volatile("" : "+v"(sc[0]), "+v"(sc[1]));
 
             // P of tile t against the reference, rounded to E4M3 in the order
             // of the P V operand: byte 4 w + i is register 4 (w & 3) + i of
             // block w >> 2.
-            const bool masked = tile_masked(t);
             float p[2][16];
 #pragma unroll
             for (int b = 0; b < 2; ++b)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     p[b][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[b][r], c_log2, -m_sub));
-                    if (masked && !visible(t, b, r))
-                        p[b][r] = 0.f;
+                    if constexpr (MASKED)
+                        p[b][r] = visible(t, b, r) ? p[b][r] : 0.f;
                 }
-            float rs0 = 0.f, rs1 = 0.f;
+            float rs0 = p[0][0], rs1 = p[0][1];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                rs0 += p[0][r];
-                rs1 += p[1][r];
+            for (int r = 2; r < 32; r += 2) {
+                rs0 += p[r >> 4][r & 15];
+                rs1 += p[r >> 4][(r & 15) + 1];
             }
             l_run += rs0 + rs1;
             i32x8 pb;
@@ -387,21 +405,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             // Scores of tile t+1 (past the end: zero rows, discarded) and P V
             // of tile t-1.
             f32x16 sn[2];
-            const int ks_next = (t + 1 < t_end) ? (int)keh[t + 1] : kE8M0One;
-            scores(knext, ks_next, sn);
+            scores(knext, ks, sn);
 #pragma unroll
             for (int db = 0; db < 4; ++db)
                 oacc[db] = mfma8(lds_pair(vprev + db * 32 * kRowsBlk + voff[0], vprev + db * 32 * kRowsBlk + voff[1]),
-                                 pb_prev, oacc[db], vs_prev, kE8M0One);
+                                 pb_prev, oacc[db], vs, kE8M0One);
 
-            float mx = kNegInf;
-            if (t + 1 < t_end) {
-                const bool nmasked = tile_masked(t + 1);
+            float mx;
+            if constexpr (NEXT_MASKED) {
+                mx = kNegInf;
 #pragma unroll
                 for (int b = 0; b < 2; ++b)
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
-                        mx = fmaxf(mx, (!nmasked || visible(t + 1, b, r)) ? sn[b][r] * c_log2 : kNegInf);
+                        mx = fmaxf(mx, visible(t + 1, b, r) ? sn[b][r] * c_log2 : kNegInf);
+            } else {  // every key visible and c_log2 > 0
+                float m0 = sn[0][0];
+#pragma unroll
+                for (int r = 1; r < 32; ++r)
+                    m0 = fmaxf(m0, sn[r >> 4][r & 15]);
+                mx = m0 * c_log2;
             }
             const bool reref = __builtin_amdgcn_ballot_w64(mx > m_thr) != 0;
 
@@ -411,7 +434,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x402, 18, 0);
+                __builtin_amdgcn_sched_group_barrier(0x402, 16, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
             asm volatile("" : "+v"(pb), "+v"(l_run));
@@ -431,7 +454,38 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             sc[0] = sn[0];
             sc[1] = sn[1];
             pb_prev = pb;
-            vs_prev = (int)veh[t];
+            ks = ks_pf;
+            vs = vs_pf;
+        };
+        using P0 = std::integral_constant<int, 0>;
+        using P1 = std::integral_constant<int, 1>;
+        using Unmasked = std::false_type;
+        using Masked = std::true_type;
+        // Tiles [0, t_free) need no mask: inside the sequence and at or below
+        // the causal diagonal of every query of the workgroup (and a positive
+        // scale, which the unmasked row max assumes).  t_free is made even so
+        // that the loops walk (buffer 0, buffer 1) pairs; the last unmasked
+        // pair is peeled because the tile after it needs the mask.
+        int t_free = N / kRowsBlk;
+        if (CAUSAL)
+            t_free = min(t_free, (q0 + 1) / kRowsBlk);
+        if (!(c_log2 > 0.f))
+            t_free = 0;
+        t_free = min(t_free, t_end) & ~1;
+        int t = 0;
+        for (; t + 2 < t_free; t += 2) {
+            step(t, P0{}, Unmasked{}, Unmasked{});
+            step(t + 1, P1{}, Unmasked{}, Unmasked{});
+        }
+        if (t < t_free) {
+            step(t, P0{}, Unmasked{}, Unmasked{});
+            step(t + 1, P1{}, Unmasked{}, Masked{});
+            t += 2;
+        }
+        for (; t < t_end; t += 2) {
+            step(t, P0{}, Masked{}, Masked{});
+            if (t + 1 < t_end)
+                step(t + 1, P1{}, Masked{}, Masked{});
         }
         // P V of the last tile.
         __builtin_amdgcn_s_waitcnt(0);
@@ -441,7 +495,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
             for (int db = 0; db < 4; ++db)
                 oacc[db] = mfma8(lds_pair(vlast + db * 32 * kRowsBlk + voff[0], vlast + db * 32 * kRowsBlk + voff[1]),
-                                 pb_prev, oacc[db], vs_prev, kE8M0One);
+                                 pb_prev, oacc[db], vs, kE8M0One);
             if (pending) {
 #pragma unroll
                 for (int b = 0; b < 4; ++b)
