@@ -24,6 +24,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
+PEAK_FP8_TFLOPS = 2 * PEAK_BF16_TFLOPS
 HBM_PEAK_GBPS = 8000.0
 METRIC = "attn fwd TFLOP/s + % of bf16 MFMA peak, 1 GPU, N=8192 d=128 causal"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_long_causal_traffic.json")
@@ -292,6 +293,98 @@ def bench_bwd(args):
     return 0
 
 
+def bench_fp8(args):
+    """One JSON line for the FP8 forward (attn_fwd_fp8) on a workload of
+    WORKLOADS (head dim 128).  Q and K are rotated with seeded random signs
+    and quantized, V quantized and transposed, once before the timed region;
+    one step is one attn_fwd_fp8 call.  The three quantization launches are
+    timed separately, and the whole path (quantize Q, K, V + attention) too."""
+    import numpy as np
+    import torch
+
+    from oracle import fp8_oracle as f8
+    from exact_io_aware_27_amd import attn, inputs
+
+    attn.load()
+    w = {x.name: x for x in inputs.WORKLOADS}[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = inputs.workload_qkv(w)
+    signs = inputs.make_signs(w.d, seed=w.seed + 1).numpy()
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    stream = torch.cuda.current_stream(dev)
+    q8, qe = attn.fp8_quantize(qd, signs=signs, stream=stream)
+    k8, ke = attn.fp8_quantize(kd, signs=signs, stream=stream)
+    vt8, ve = attn.fp8_quantize(vd, transpose=True, stream=stream)
+    od = torch.empty_like(qd)
+    lsed = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    eff = w.scale / w.d  # the rotation multiplies Q K^T by d
+
+    def attend():
+        attn.attn_fwd_fp8(q8, k8, vt8, qe, ke, ve, od, lsed, w.B, w.H, w.N, w.d, w.causal, eff, stream)
+
+    def quantize():
+        attn.fp8_quantize_status(qd, w.B, w.H, w.N, w.d, False, signs, q8, qe, stream)
+        attn.fp8_quantize_status(kd, w.B, w.H, w.N, w.d, False, signs, k8, ke, stream)
+        attn.fp8_quantize_status(vd, w.B, w.H, w.N, w.d, True, None, vt8, ve, stream)
+
+    def timed(fn, steps):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    qms = timed(quantize, max(1, args.steps // 2))
+    ms = timed(attend, args.steps)  # last: od and lsed hold the result
+    tflops = w.flops / (ms * 1e-3) / 1e12
+    out = {"metric": "attn fwd FP8 TFLOP/s + % of fp8 MFMA peak, 1 GPU", "value": round(tflops, 2),
+           "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "fp8-e4m3", "data": "synthetic",
+           "config": {"workload": w.describe() + " fp8 (block 64, incoherent processing)", "B": w.B, "H": w.H,
+                      "N": w.N, "d": w.d, "causal": w.causal, "scale": w.scale, "seed": w.seed},
+           "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": round(PEAK_FP8_TFLOPS, 1),
+                        "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP8_TFLOPS, 4), "traffic": None},
+           "quantize_ms": round(qms, 5),
+           "with_quantize_TFLOPs": round(w.flops / ((ms + qms) * 1e-3) / 1e12, 2)}
+    if args.cpu_rows > 0:
+        # the oracle's FP8 method on a row sample of one head: quantize the head
+        # (rotation, blocks), then exact attention of the dequantized operands
+        R = min(args.cpu_rows, w.N)
+        rows = inputs.row_subset(w.N, R, w.seed, 0, (0, w.N - 1)).numpy()
+        t0 = time.perf_counter()
+        prep = f8.prepare_fp8(q[:1, :1], k[:1, :1], v[:1, :1], signs=signs)
+        o_ref, lse_ref, sig = [], [], []
+        for r in rows:
+            hi = r + 1 if w.causal else w.N
+            a, b_, c = f8.attention_fp64(prep["q"][:, :, [r]], prep["k"][:, :, :hi], prep["v"][:, :, :hi], False,
+                                         w.scale / prep["qk_factor"], p_rounding=True)
+            o_ref.append(a), lse_ref.append(b_), sig.append(c)
+        dt = time.perf_counter() - t0
+        o_ref, lse_ref, sig = (np.concatenate(x, axis=2) for x in (o_ref, lse_ref, sig))
+        keys = (rows + 1).sum() if w.causal else len(rows) * w.N
+        flops = float(keys) * 4 * w.d
+        og = od[0, 0, rows].double().cpu().numpy()[None, None]
+        z = (og - o_ref) / np.sqrt(sig ** 2 + 1e-10)
+        out["cpu_baseline"] = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+                               "sample": "head (0, 0): quantization of the whole head, then %d seeded query rows "
+                                         "against every visible key; %.3g counted flops in %.1f s" % (R, flops, dt)}
+        out["parity_sampled_rows"] = {"rows": int(R), "mean_z2": float(np.mean(z ** 2)),
+                                      "max_abs_z": float(np.abs(z).max()),
+                                      "max_abs_dLSE": float(np.abs(lsed[0, 0, rows].double().cpu().numpy()
+                                                                   - lse_ref[0, 0]).max())}
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -305,6 +398,7 @@ def main():
                     help="measure attn_fwd_splitkv on a workload of exact_io_aware_27_amd.inputs.SPLITKV_WORKLOADS")
     ap.add_argument("--splits", type=int, default=0, help="key ranges for --splitkv (0: the workload's)")
     ap.add_argument("--bwd", action="store_true", help="measure the backward pass (attn_bwd) on --workload")
+    ap.add_argument("--fp8", action="store_true", help="measure the FP8 forward (attn_fwd_fp8) on --workload")
     ap.add_argument("--cpu-heads", type=int, default=1,
                     help="--bwd: whole heads in the oracle's CPU-baseline sample (0: skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -328,6 +422,8 @@ def main():
         return bench_splitkv(args)
     if args.bwd:
         return bench_bwd(args)
+    if args.fp8:
+        return bench_fp8(args)
 
     import torch
 
