@@ -24,8 +24,8 @@
 // atomics); in exchange there is no atomic traffic and no dQ workspace.
 //
 // gfx950 mapping (shared by both kernels)
-//   * 4 waves per workgroup, 32 rows (queries or keys) per wave, two
-//     workgroups per CU.  Each lane owns one row of its wave (lane % 32) in
+//   * 32 rows (queries or keys) per wave; 8 waves per workgroup for d = 128
+//     (one per CU), 4 for d = 64 (two per CU).  Each lane owns one row of its wave (lane % 32) in
 //     the 32x32 accumulator layout of v_mfma_f32_32x32x16_bf16 and 16 of the
 //     32 columns of the other side.
 //   * The operands walked by the loop (K and V in the dQ kernel, Q and dO in
@@ -44,20 +44,26 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "attn_common.h"
 #include "attn_launch.h"
 
 namespace attn_gfx950 {
 namespace bwd {
 
-constexpr int kRows = 32;   // rows per wave
-constexpr int kWaves = 4;   // waves per workgroup
-constexpr int kThreads = kWave * kWaves;
-constexpr int kBlock = kRows * kWaves;  // rows (queries or keys) a workgroup owns
-constexpr int kTile = 64;   // rows per LDS tile of the walked operands
+constexpr int kRows = 32;     // rows per wave
+constexpr int kBlockMin = 128;  // fewest rows (queries or keys) a workgroup owns
+constexpr int kTile = 64;     // rows per LDS tile of the walked operands
 
+// Workgroup shape per head dim, as in the forward pass: d = 128 runs 8 waves
+// (one workgroup per CU), so each tile copied into LDS serves 256 rows; d = 64
+// runs 4 waves, two workgroups per CU.  Either way two waves share a SIMD.
 template <int D>
 struct Shape {
+    static constexpr int kWaves = D == 128 ? 8 : 4;
+    static constexpr int kThreads = kWave * kWaves;
+    static constexpr int kBlock = kRows * kWaves;         // rows a workgroup owns
     static constexpr int kRowBytes = D * 2;
     static constexpr int kChunks = D / 8;                 // 16-byte chunks per row
     static constexpr int kBytes = kTile * kRowBytes;      // one tile
@@ -144,6 +150,19 @@ struct Offsets {
                 const int dcol = 32 * b + 16 * (g & 1) + 4 * (i & 3);
                 tr[b][jj] = lds_off<D>(r, dcol >> 3) + ((dcol & 4) << 1);
             }
+    }
+
+    // Make the offsets opaque to the optimiser at the start of a tile, so that
+    // their sums with each buffer's constant base are not hoisted out of the
+    // loop as separate registers instead of riding in the LDS read offset.
+    __device__ __forceinline__ void opaque()
+    {
+#pragma unroll
+        for (int st = 0; st < S::kSteps; ++st)
+            asm volatile("" : "+v"(row[st]));
+#pragma unroll
+        for (int b = 0; b < S::kDBlocks; ++b)
+            asm volatile("" : "+v"(tr[b][0]), "+v"(tr[b][1]));
     }
 };
 
@@ -254,7 +273,7 @@ __device__ __forceinline__ int pair_block(bool causal, int nblk, int unit, int p
 // block: S^T = K Q^T and dP^T = V dO^T (keys x queries), P^T = exp2(S^T
 // c_log2 - L2), dS^T = P^T (dP^T - D), dQ^T += K^T dS^T.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dq_kernel(
+__global__ __launch_bounds__(Shape<D>::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dq_kernel(
     const BArgs a)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -268,7 +287,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const int n = lane & 31, half = lane >> 5;
     const int N = a.N, nblk = a.ntiles;
-    const Offsets<D> off(wave, lane);
+    Offsets<D> off(wave, lane);
 
     const int n_units = CAUSAL ? (nblk + 1) / 2 : nblk;
     int bh, unit;
@@ -280,12 +299,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int pass = 0; pass < npass; ++pass) {
         if (pass > 0)
             __syncthreads();  // every wave is done with the previous block's LDS
-        const int q0 = pair_block(CAUSAL, nblk, unit, pass) * kBlock;
-        const int qw0 = q0 + wave * kRows;
+        const int q0 = pair_block(CAUSAL, nblk, unit, pass) * S::kBlock;
+        const int qw0 = q0 + wave_u * kRows;
         const int qidx = qw0 + n;
         const bool q_ok = qidx < N;
         const bool wave_live = qw0 < N;
-        const int kv_end = CAUSAL ? min(N, q0 + kBlock) : N;
+        const int kv_end = CAUSAL ? min(N, q0 + S::kBlock) : N;
         const int t_end = (kv_end + kTile - 1) / kTile;
 
         load_tile<D>(Kh, kv_end, 0, sk0, wave_u, off.dma);
@@ -320,11 +339,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        for (int t = 0; t < t_end; ++t) {
-            char *kc = (t & 1) ? sk1 : sk0, *vc = (t & 1) ? sv1 : sv0;
+        // One 64-key tile t in buffer set P = t % 2 (compile-time, so that the
+        // buffer addresses fold into the LDS read offsets).
+        auto tile = [&](int t, auto parity_tag) __attribute__((always_inline)) {
+            constexpr int P = decltype(parity_tag)::value;
+            char *kc = P ? sk1 : sk0, *vc = P ? sv1 : sv0;
+            off.opaque();
             if (t + 1 < t_end) {  // the other buffers were released by the last barrier
-                load_tile<D>(Kh, kv_end, (t + 1) * kTile, (t & 1) ? sk0 : sk1, wave_u, off.dma);
-                load_tile<D>(Vh, kv_end, (t + 1) * kTile, (t & 1) ? sv0 : sv1, wave_u, off.dma);
+                load_tile<D>(Kh, kv_end, (t + 1) * kTile, P ? sk0 : sk1, wave_u, off.dma);
+                load_tile<D>(Vh, kv_end, (t + 1) * kTile, P ? sv0 : sv1, wave_u, off.dma);
             }
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
@@ -340,20 +363,40 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 // Register 4 j + e holds key key0 + 8 j + 4 half + e.  Keys past
                 // N have zero K and V rows: their dS multiplies a zero K row.
                 const bool masked = CAUSAL && key0 + kRows - 1 > qw0;
-                float ds[16];
+                float p[16], ds[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.c_log2, -l2));
-                    if (masked && key0 + 8 * (r >> 2) + 4 * half + (r & 3) > qidx)
-                        p = 0.f;
-                    ds[r] = p * (dp[r] - dsum);
+                    p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.c_log2, -l2));
+                    p[r] = (masked & (key0 + 8 * (r >> 2) + 4 * half + (r & 3) > qidx)) ? 0.f : p[r];
                 }
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    ds[r] = p[r] * (dp[r] - dsum);
                 bf16x8 dsb[2];
                 pack_b(ds, dsb);
                 tr_times<D>(dq, kbase, off, dsb);
+                // The exps need only S: they run under the dP products.  Operand
+                // reads stay about two products ahead.
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+                for (int i = 0; i < S::kSteps; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // S
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                }
+#pragma unroll
+                for (int i = 0; i < S::kSteps; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // dP
+                    __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
             }
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
+        };
+        for (int t = 0; t < t_end; t += 2) {
+            tile(t, std::integral_constant<int, 0>{});
+            if (t + 1 < t_end)
+                tile(t + 1, std::integral_constant<int, 1>{});
         }
         if (q_ok)
             store_rows<D>(a.dQ + head + (size_t)qidx * D, dq, a.scale, half);
@@ -366,7 +409,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 // S = Q K^T and dP = dO V^T (queries x keys), P = exp2(S c_log2 - L2),
 // dS = P (dP - D), dV^T += dO^T P, dK^T += Q^T dS.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dkdv_kernel(
+__global__ __launch_bounds__(Shape<D>::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dkdv_kernel(
     const BArgs a)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -381,7 +424,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const int n = lane & 31, half = lane >> 5;
     const int N = a.N, nblk = a.ntiles;
-    const Offsets<D> off(wave, lane);
+    Offsets<D> off(wave, lane);
 
     const int n_units = CAUSAL ? (nblk + 1) / 2 : nblk;
     int bh, unit;
@@ -404,8 +447,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int pass = 0; pass < npass; ++pass) {
         if (pass > 0)
             __syncthreads();
-        const int k0 = pair_block(CAUSAL, nblk, unit, pass) * kBlock;
-        const int kw0 = k0 + wave * kRows;
+        const int k0 = pair_block(CAUSAL, nblk, unit, pass) * S::kBlock;
+        const int kw0 = k0 + wave_u * kRows;
         const int kidx = kw0 + n;
         const bool k_ok = kidx < N;
         const bool wave_live = kw0 < N;
@@ -433,10 +476,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        for (int t = t_lo; t < t_end; ++t) {
-            const bool second = ((t - t_lo) & 1) != 0;
+        // One 64-query tile t in buffer set P = (t - t_lo) % 2 (compile-time, so
+        // that the buffer addresses fold into the LDS read offsets).
+        auto tile = [&](int t, auto parity_tag) __attribute__((always_inline)) {
+            constexpr bool second = decltype(parity_tag)::value != 0;
             const char *qc = second ? sq1 : sq0, *gc = second ? sg1 : sg0;
             const float *lc = second ? sl1 : sl0, *dc = second ? sd1 : sd0;
+            off.opaque();
             if (t + 1 < t_end)
                 load_all(t + 1, !second);
 #pragma unroll
@@ -464,8 +510,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                     for (int e = 0; e < 4; ++e) {
                         const int r = 4 * j + e;
                         float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.c_log2, -l4[e]));
-                        if (masked && qs0 + 8 * j + 4 * half + e < kidx)
-                            pr = 0.f;
+                        pr = (masked & (qs0 + 8 * j + 4 * half + e < kidx)) ? 0.f : pr;
                         p[r] = pr;
                         ds[r] = pr * (dp[r] - d4[e]);
                     }
@@ -478,6 +523,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             }
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
+        };
+        for (int t = t_lo; t < t_end; t += 2) {
+            tile(t, std::integral_constant<int, 0>{});
+            if (t + 1 < t_end)
+                tile(t + 1, std::integral_constant<int, 1>{});
         }
         if (k_ok) {
             store_rows<D>(a.dK + head + (size_t)kidx * D, dk, a.scale, half);
@@ -504,15 +554,16 @@ static hipError_t launch(const AttnBwdLaunch &l)
     a.dV = (__bf16 *)l.dv;
     a.BH = (int)l.BH;
     a.N = (int)l.N;
-    a.ntiles = (int)((l.N + kBlock - 1) / kBlock);
+    using S = Shape<D>;
+    a.ntiles = (int)((l.N + S::kBlock - 1) / S::kBlock);
     a.n_wg = (int)(l.BH * (CAUSAL ? (a.ntiles + 1) / 2 : a.ntiles));
     a.c_log2 = l.scale * kLog2e;
     a.scale = l.scale;
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL>), dim3(a.n_wg), dim3(kThreads), 0, l.stream, a);
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL>), dim3(a.n_wg), dim3(S::kThreads), 0, l.stream, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL>), dim3(a.n_wg), dim3(kThreads), 0, l.stream, a);
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL>), dim3(a.n_wg), dim3(S::kThreads), 0, l.stream, a);
     return hipGetLastError();
 }
 
@@ -521,7 +572,7 @@ static hipError_t launch(const AttnBwdLaunch &l)
 
 int64_t attn_bwd_workgroups(int64_t BH, int64_t N)
 {
-    return BH * ((N + attn_gfx950::bwd::kBlock - 1) / attn_gfx950::bwd::kBlock);
+    return BH * ((N + attn_gfx950::bwd::kBlockMin - 1) / attn_gfx950::bwd::kBlockMin);
 }
 
 hipError_t attn_bwd_launch(const AttnBwdLaunch &l)
