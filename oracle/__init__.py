@@ -18,5 +18,5 @@ library never imports it; the two share no code.
   of the recurrence against the definition.
 """
 
-from .oracle import attention, attention_bwd, build, library_path  # noqa: F401
+from .oracle import attention, attention_bwd, attention_bwd_dq_rows, build, library_path  # noqa: F401
 from .online import merge_partials, online_attention  # noqa: F401

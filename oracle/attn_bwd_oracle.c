@@ -189,3 +189,110 @@ int oracle_attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, con
     pthread_mutex_destroy(&c.lock);
     return c.status;
 }
+
+/*
+ * oracle_attn_bwd_dq_rows: dQ_i (and D_i) for R given query rows i of every
+ * head, by the same per-row steps as oracle_attn_bwd: O(Nk d) per row, so
+ * rows of long sequences can be checked one by one (dK and dV need every row).
+ *   rows   int64 [BH][R] query indices;  dq: out fp64 [BH][R][d];  dsum: out [BH][R]
+ *   term2  out fp64 [BH][R][d] or NULL: sum_j (scale dS_ij k_jt)^2, the sum of
+ *          squared terms of each dQ element (the scale of its rounding error
+ *          when every dS_ij is rounded before the product)
+ *   pk, o  out fp64 [BH][R][d] or NULL: sum_j P_ij k_jt and the output row
+ *          O_i = sum_j P_ij v_j (a change dD of D_i moves dQ_i by
+ *          -scale dD (P K)_i, and D is formed from O)
+ *   pv2    out fp64 [BH][R][d] or NULL: sum_j P_ij^2 (v_jt - O_it)^2, the
+ *          scale of the error the forward pass's rounding of P puts into O
+ */
+int oracle_attn_bwd_dq_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *dout,
+                            int64_t BH, int64_t Nq, int64_t Nk, int64_t d, int causal, double scale,
+                            const int64_t *rows, int64_t R, double *dq, double *dsum, double *term2,
+                            double *pk, double *o, double *pv2)
+{
+    if (!q || !k || !v || !dout || !rows || !dq || !dsum || BH < 0 || Nq < 1 || Nk < 1 || d < 1 || R < 0 ||
+        !isfinite(scale) || (causal && Nq > Nk))
+        return BWD_BAD_ARG;
+    double *S = malloc((size_t)Nk * sizeof(double));
+    double *P = malloc((size_t)Nk * sizeof(double));
+    double *dP = malloc((size_t)Nk * sizeof(double));
+    if (!S || !P || !dP) {
+        free(S); free(P); free(dP);
+        return BWD_NO_MEMORY;
+    }
+    int status = BWD_OK;
+    for (int64_t bh = 0; bh < BH && status == BWD_OK; ++bh) {
+        const uint16_t *qh = q + bh * Nq * d, *gh = dout + bh * Nq * d;
+        const uint16_t *kh = k + bh * Nk * d, *vh = v + bh * Nk * d;
+        for (int64_t x = 0; x < R; ++x) {
+            const int64_t i = rows[bh * R + x];
+            if (i < 0 || i >= Nq) {
+                status = BWD_BAD_ARG;
+                break;
+            }
+            const int64_t nkeys = causal ? i + (Nk - Nq) + 1 : Nk;
+            double m = -INFINITY;
+            for (int64_t j = 0; j < nkeys; ++j) {
+                double dot = 0.0;
+                for (int64_t t = 0; t < d; ++t)
+                    dot += widen(qh[i * d + t]) * widen(kh[j * d + t]);
+                S[j] = scale * dot;
+                if (S[j] > m)
+                    m = S[j];
+            }
+            double l = 0.0;
+            for (int64_t j = 0; j < nkeys; ++j) {
+                P[j] = exp(S[j] - m);
+                l += P[j];
+            }
+            double Di = 0.0;
+            for (int64_t j = 0; j < nkeys; ++j) {
+                P[j] /= l;
+                double dot = 0.0;
+                for (int64_t t = 0; t < d; ++t)
+                    dot += widen(gh[i * d + t]) * widen(vh[j * d + t]);
+                dP[j] = dot;
+                Di += P[j] * dP[j];
+            }
+            dsum[bh * R + x] = Di;
+            double *out = dq + (bh * R + x) * d;
+            double *t2 = term2 ? term2 + (bh * R + x) * d : NULL;
+            double *pko = pk ? pk + (bh * R + x) * d : NULL;
+            double *oo = o ? o + (bh * R + x) * d : NULL;
+            double *p2 = pv2 ? pv2 + (bh * R + x) * d : NULL;
+            for (int64_t t = 0; t < d; ++t) {
+                out[t] = 0.0;
+                if (t2)
+                    t2[t] = 0.0;
+                if (pko)
+                    pko[t] = 0.0;
+                if (oo)
+                    oo[t] = 0.0;
+            }
+            for (int64_t j = 0; j < nkeys; ++j) {
+                const double ds = P[j] * (dP[j] - Di);
+                for (int64_t t = 0; t < d; ++t) {
+                    const double kt = widen(kh[j * d + t]);
+                    const double term = scale * ds * kt;
+                    out[t] += term;
+                    if (t2)
+                        t2[t] += term * term;
+                    if (pko)
+                        pko[t] += P[j] * kt;
+                    if (oo)
+                        oo[t] += P[j] * widen(vh[j * d + t]);
+                }
+            }
+            if (p2 && oo) {  /* second pass: O is known now */
+                for (int64_t t = 0; t < d; ++t)
+                    p2[t] = 0.0;
+                for (int64_t j = 0; j < nkeys; ++j)
+                    for (int64_t t = 0; t < d; ++t) {
+                        const double dv = widen(vh[j * d + t]) - oo[t];
+                        p2[t] += P[j] * P[j] * dv * dv;
+                    }
+            }
+        }
+    }
+    free(S); free(P); free(dP);
+    return status;
+}

@@ -82,6 +82,9 @@ def load_bwd_library(path):
     i64 = ctypes.c_int64
     f.argtypes = [p, p, p, p, i64, i64, i64, i64, ctypes.c_int, ctypes.c_double,
                   p, p, p, p, ctypes.c_int]
+    g = lib.oracle_attn_bwd_dq_rows
+    g.restype = ctypes.c_int
+    g.argtypes = [p, p, p, p, i64, i64, i64, i64, ctypes.c_int, ctypes.c_double, p, i64, p, p, p, p, p, p]
     return lib
 
 
@@ -184,3 +187,36 @@ def attention_bwd(q, k, v, do, causal, scale, nthreads=None, lib=None):
         raise RuntimeError("oracle_attn_bwd failed: %s" % ORACLE_STATUS.get(st, st))
     return (dq.reshape(B, H, Nq, d), dk.reshape(B, H, Nk, d), dv.reshape(B, H, Nk, d),
             dsum.reshape(B, H, Nq))
+
+
+def attention_bwd_dq_rows(q, k, v, do, causal, scale, rows, lib=None, with_terms=False):
+    """dQ (and D) of the query rows `rows` (int array [B*H, R] or [B, H, R])
+    of every head, fp64, row by row.  Returns (dq [B, H, R, d], dsum [B, H, R])
+    and, with_terms, term2, pk, o, pv2 [B, H, R, d]: sum_j (scale dS_ij k_jt)^2,
+    sum_j P_ij k_jt, the output row O_i and sum_j P_ij^2 (v_jt - O_it)^2."""
+    qb, kb, vb, gb = _bf16_bits(q), _bf16_bits(k), _bf16_bits(v), _bf16_bits(do)
+    B, H, Nq, d = qb.shape
+    Nk = kb.shape[2]
+    BH = B * H
+    rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(BH, -1))
+    R = rows_arr.shape[1]
+    dq = np.empty((BH, R, d), dtype=np.float64)
+    dsum = np.empty((BH, R), dtype=np.float64)
+    term2 = np.empty((BH, R, d), dtype=np.float64) if with_terms else None
+    pk = np.empty((BH, R, d), dtype=np.float64) if with_terms else None
+    o = np.empty((BH, R, d), dtype=np.float64) if with_terms else None
+    pv2 = np.empty((BH, R, d), dtype=np.float64) if with_terms else None
+    lib = lib or _load_bwd()
+    st = lib.oracle_attn_bwd_dq_rows(qb.ctypes.data, kb.ctypes.data, vb.ctypes.data, gb.ctypes.data, BH, Nq, Nk,
+                                     d, 1 if causal else 0, float(scale), rows_arr.ctypes.data, R,
+                                     dq.ctypes.data, dsum.ctypes.data,
+                                     None if term2 is None else term2.ctypes.data,
+                                     None if pk is None else pk.ctypes.data,
+                                     None if o is None else o.ctypes.data,
+                                     None if pv2 is None else pv2.ctypes.data)
+    if st != 0:
+        raise RuntimeError("oracle_attn_bwd_dq_rows failed: %s" % ORACLE_STATUS.get(st, st))
+    out = (dq.reshape(B, H, R, d), dsum.reshape(B, H, R))
+    if with_terms:
+        out = out + tuple(x.reshape(B, H, R, d) for x in (term2, pk, o, pv2))
+    return out

@@ -112,3 +112,41 @@ def assert_grad_parity(rep, what=""):
     assert rep["finite"], "%s: non-finite gradient %s" % (what, rep)
     assert rep["max_rel"] <= GRAD_MAX_REL, "%s: max|d| over 2e-2 max|ref|: %s" % (what, rep)
     assert rep["mean_rel"] <= GRAD_MEAN_REL, "%s: mean|d| over 1e-2 mean|ref|: %s" % (what, rep)
+
+
+# Long sums.  The per-head bar above assumes the rounding error of a gradient
+# element stays a few u of the tensor's scale; for rows that sum 65536 terms
+# whose total nearly cancels (each row of dS sums to zero) the random rounding
+# of every term (dS_ij to bf16, relative error uniform within +-2^-9) grows
+# like the root of the sum of squared terms instead: 2^-9 / sqrt(3) *
+# sqrt(sum_j term_jt^2) (from the oracle, per element).  D_i = dO_i . O_i is
+# formed from the forward pass's O, whose error is its own bf16 rounding of P
+# before P V (variance 2^-18/3 sum_j P_ij^2 (v_jt - O_it)^2) plus the bf16
+# rounding of O itself (halfulp(O_it)^2 / 3): that moves D_i by sigma_D^2 =
+# sum_t dO_it^2 (both variances) and dQ_i by -scale dD (P K)_i, coherently
+# over the row.  With one bf16 rounding of the output, sigma is the root of the sum of
+# the three variances: the mean of (d / sigma)^2 must stay near 1 (<= 2) and
+# no element may pass 6 sigma.
+def compare_grad_model(g_gpu, ref, term2, pk=None, o=None, dout=None, scale=0.0, pv2=None):
+    """g_gpu: bf16 [B, H, R, d]; ref, term2, pk, o, pv2: oracle rows
+    [B, H, R, d]; dout: the rows' upstream gradient [B, H, R, d]."""
+    g = g_gpu.detach().float().cpu().numpy().astype(np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    out_round = bf16_half_ulp(np.maximum(np.abs(ref), np.abs(g)))
+    var = (2.0 ** -9) ** 2 / 3 * np.asarray(term2) + out_round ** 2 / 3 + 1e-12
+    if pk is not None:
+        o_var = bf16_half_ulp(np.asarray(o)) ** 2 / 3
+        if pv2 is not None:
+            o_var = o_var + (2.0 ** -9) ** 2 / 3 * np.asarray(pv2)
+        sig_d2 = np.sum(np.asarray(dout, dtype=np.float64) ** 2 * o_var, axis=-1, keepdims=True)
+        var = var + scale ** 2 * sig_d2 * np.asarray(pk) ** 2
+    sigma = np.sqrt(var)
+    z = (g - ref) / sigma
+    return dict(mean_z2=float(np.mean(z ** 2)), max_abs_z=float(np.abs(z).max()),
+                max_abs=float(np.abs(g - ref).max()), finite=bool(np.isfinite(g).all()))
+
+
+def assert_grad_model(rep, what=""):
+    assert rep["finite"], "%s: non-finite gradient %s" % (what, rep)
+    assert rep["mean_z2"] <= 2.0, "%s: mean (d/sigma)^2 over 2: %s" % (what, rep)
+    assert rep["max_abs_z"] <= 6.0, "%s: |d| over 6 sigma: %s" % (what, rep)

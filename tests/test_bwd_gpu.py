@@ -169,3 +169,28 @@ def test_single_key_closed_form():
     dq, dk, dv = run(q, k, v, g, True, 0.125)
     assert float(dq.float().abs().max()) < 1e-4 and float(dk.float().abs().max()) < 1e-4
     assert torch.equal(dv.cpu().view(torch.int16), g.view(torch.int16))
+
+
+@pytest.mark.parametrize("d,causal", [(128, True), (64, False)])
+def test_very_long_sequence_sampled_dq_rows_and_identities(d, causal):
+    """N = 65536: sampled dQ rows element by element against the oracle's
+    row-by-row entry (O(N d) per row), held to the rounding model of long sums
+    (tests/parity.py, compare_grad_model), and for dK and dV the identities
+    that hold at any size."""
+    B, H, N = 1, 2, 65536
+    q, k, v, g = case(B, H, N, d, seed=3400 + d)
+    scale = 1.0 / math.sqrt(d)
+    say("case: very long", (B, H, N, d), "causal" if causal else "non-causal")
+    dq, dk, dv = run(q, k, v, g, causal, scale)
+    rows = torch.stack([inputs.row_subset(N, 24, 3400, bh, (0, 1, N - 1)) for bh in range(B * H)])
+    rq, _, term2, pk, o, pv2 = oracle.attention_bwd_dq_rows(q, k, v, g, causal, scale, rows.numpy(),
+                                                            with_terms=True)
+    g_rows = parity.gather_rows(g, rows).double().numpy()
+    rep = parity.compare_grad_model(parity.gather_rows(dq, rows), rq, term2, pk, o, g_rows, scale, pv2)
+    say("   sampled dQ rows", rep)
+    parity.assert_grad_model(rep, "very long dQ rows")
+    dk64, dv64 = dk.double(), dv.double()
+    ksum = dk64.sum(dim=2).abs() / dk64.abs().sum(dim=2).clamp_min(1e-30)
+    vsum = (dv64.sum(dim=2) - g.to(DEV).double().sum(dim=2)).abs() / dv64.abs().sum(dim=2).clamp_min(1e-30)
+    say("   invariants: max rel |sum dK| %.3g, max rel |sum dV - sum dO| %.3g" % (ksum.max(), vsum.max()))
+    assert float(ksum.max()) < 1e-2 and float(vsum.max()) < 1e-2

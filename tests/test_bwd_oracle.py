@@ -173,6 +173,18 @@ def test_matches_autograd_float64(B, H, Nq, Nk, d, causal):
     np.testing.assert_allclose(dsum, (o * g.double().numpy()).sum(-1), rtol=0, atol=1e-12)
 
 
+def test_dq_rows_equal_the_whole_head_oracle():
+    # the row-by-row entry against the pinned whole-head one (same steps per row)
+    q, k, v, g = _case(2, 1, 97, 97, 64, 650)
+    rows = np.array([[0, 5, 63, 64, 96], [96, 1, 2, 50, 77]])
+    for causal in (False, True):
+        dq, _, _, dsum = oracle.attention_bwd(q, k, v, g, causal, 0.2)
+        rq, rd = oracle.attention_bwd_dq_rows(q, k, v, g, causal, 0.2, rows)
+        for bh in range(2):
+            np.testing.assert_array_equal(rq[bh, 0], dq[bh, 0, rows[bh]])
+            np.testing.assert_array_equal(rd[bh, 0], dsum[bh, 0, rows[bh]])
+
+
 def test_single_key_has_no_logit_gradient():
     # one key: P = 1 whatever the logits, so dQ = dK = 0 and dV = sum_i dO_i
     q, k, v, g = _case(1, 1, 17, 1, 64, 700)
@@ -237,6 +249,60 @@ def test_unmodified_source_passes_the_suite(bwd_source, tmp_path):
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(name, bwd_source, tmp_path):
     old, new = MUTANTS[name]
-    assert bwd_source.count(old) == 1, "mutation site not found: %r" % old
+    # a slip is planted at every site it can occur (the whole-head and the
+    # row-by-row entries share their per-row steps)
+    assert bwd_source.count(old) >= 1, "mutation site not found: %r" % old
     lib = _build(bwd_source.replace(old, new), str(tmp_path / ("libbwd_%s.so" % name)))
     assert _pins(lib), "no pin caught mutant %s" % name
+
+
+def test_long_sum_rounding_model_matches_actual_bf16_rounding_of_ds():
+    """The error model the long-sequence GPU test uses: rounding every dS_ij
+    to bf16 before dQ = scale dS K moves dQ_t by a zero-mean error of
+    standard deviation 2^-9/sqrt(3) * sqrt(sum_j term_jt^2).  Checked against
+    the actual rounding (dS computed here in fp64, rounded with PyTorch)."""
+    q, k, v, g = _case(1, 1, 600, 600, 64, 660)
+    scale = 0.125
+    rows = np.array([[5, 100, 333, 599]])
+    rq, _, term2, pk, o, _ = oracle.attention_bwd_dq_rows(q, k, v, g, True, scale, rows, with_terms=True)
+    qd, kd, vd, gd = (x.double().numpy()[0, 0] for x in (q, k, v, g))
+    z = []
+    for x, i in enumerate(rows[0]):
+        s = scale * kd[:i + 1] @ qd[i]
+        p = np.exp(s - s.max())
+        p /= p.sum()
+        dp = vd[:i + 1] @ gd[i]
+        ds = p * (dp - p @ dp)
+        ds_r = torch.from_numpy(ds).to(torch.bfloat16).double().numpy()
+        dq_r = scale * ds_r @ kd[:i + 1]
+        z.append((dq_r - rq[0, 0, x]) / np.sqrt((2.0 ** -9) ** 2 / 3 * term2[0, 0, x]))
+    z = np.concatenate(z)
+    assert 0.2 < float(np.mean(z ** 2)) < 1.5, float(np.mean(z ** 2))
+
+
+
+def test_d_rounding_model_matches_actual_bf16_rounding_of_o():
+    """The second term of that model: D formed from O rounded to bf16 moves
+    dQ_i by -scale dD (P K)_i.  Checked against D from the actually rounded O
+    (rows whose P is concentrated, where the term matters most)."""
+    q, k, v, g = _case(1, 1, 300, 300, 64, 661)
+    q = q * 4  # large logits: P concentrated on few keys
+    scale = 0.125
+    rows = np.array([[10, 150, 299]])
+    rq, rd, _, pk, o, _ = oracle.attention_bwd_dq_rows(q, k, v, g, True, scale, rows, with_terms=True)
+    gd = g.double().numpy()[0, 0]
+    z = []
+    for x, i in enumerate(rows[0]):
+        o_r = torch.from_numpy(o[0, 0, x]).to(torch.bfloat16).double().numpy()
+        dD = gd[i] @ o_r - rd[0, 0, x]
+        shift = -scale * dD * pk[0, 0, x]
+        half = parity_half_ulp(o[0, 0, x])
+        sig = scale * np.sqrt(np.sum(gd[i] ** 2 * half ** 2 / 3)) * np.abs(pk[0, 0, x])
+        z.append(shift / sig)
+    z = np.concatenate(z)
+    assert float(np.mean(z ** 2)) < 4.0 and np.all(np.isfinite(z))
+
+
+def parity_half_ulp(x):
+    _, e = np.frexp(np.abs(x))
+    return np.where(x == 0, 0.0, np.ldexp(1.0, e - 9))
