@@ -163,3 +163,47 @@ def _causal_rows(prep, rows, scale):
                               scale / prep["qk_factor"], p_rounding=True) for r in rows]
     return (np.concatenate([x[0] for x in outs], axis=2), np.concatenate([x[1] for x in outs], axis=2),
             np.concatenate([x[2] for x in outs], axis=2))
+
+
+def test_very_long_sequence_sampled_rows():
+    """N = 65536 causal, one batch of two heads: sampled query rows of both
+    heads against the oracle, each over its whole visible prefix."""
+    from exact_io_aware_27_amd import attn
+    B, H, N, d = 1, 2, 65536, 128
+    q, k, v = inputs.make_qkv(B, H, N, d, seed=4400)
+    signs = inputs.make_signs(d, seed=4401).numpy()
+    scale = 1.0 / math.sqrt(d)
+    say("case: very long fp8", (B, H, N, d))
+    o, lse = attn.attention_fp8(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, scale=scale, signs=signs)
+    torch.cuda.synchronize()
+    for h in range(H):
+        sl = (slice(0, 1), slice(h, h + 1))
+        prep = f8.prepare_fp8(q[sl], k[sl], v[sl], signs=signs)
+        rows = inputs.row_subset(N, 12, 4400, h, (0, 63, 64, N - 1)).numpy()
+        o_ref, lse_ref, sigma = _causal_rows(prep, rows, scale)
+        og = o[0, h, rows].double().cpu().numpy()[None, None]
+        rounding = parity.bf16_half_ulp(np.maximum(np.abs(o_ref), np.abs(og)))
+        z = (og - o_ref) / np.sqrt(sigma ** 2 + rounding ** 2 / 3 + 1e-10)
+        dl = np.abs(lse[0, h, rows].double().cpu().numpy() - lse_ref[0, 0])
+        say("   head %d: mean z^2 %.3f, max |z| %.2f, max |dLSE| %.2e" % (h, np.mean(z ** 2), np.abs(z).max(), dl.max()))
+        assert np.mean(z ** 2) <= 2.0 and np.abs(z).max() <= 6.0 and dl.max() <= 1e-3
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.05])
+def test_non_positive_scale(scale):
+    """scale <= 0 takes the path where every tile is masked (the unmasked
+    row max assumes a positive scale): the results must still match."""
+    from exact_io_aware_27_amd import attn
+    B, H, N, d = 1, 2, 300, 128
+    q, k, v = inputs.make_qkv(B, H, N, d, seed=4500)
+    say("case: fp8 scale", scale)
+    o, lse = attn.attention_fp8(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, scale=scale)
+    torch.cuda.synchronize()
+    prep = f8.prepare_fp8(q, k, v)
+    o_ref, lse_ref, sigma = f8.attention_fp64(prep["q"], prep["k"], prep["v"], True, scale, p_rounding=True)
+    og = o.double().cpu().numpy()
+    rounding = parity.bf16_half_ulp(np.maximum(np.abs(o_ref), np.abs(og)))
+    z = (og - o_ref) / np.sqrt(sigma ** 2 + rounding ** 2 / 3 + 1e-10)
+    dl = np.abs(lse.double().cpu().numpy() - lse_ref)
+    say("   mean z^2 %.3f, max |z| %.2f, max |dLSE| %.2e" % (np.mean(z ** 2), np.abs(z).max(), dl.max()))
+    assert np.mean(z ** 2) <= 2.0 and np.abs(z).max() <= 6.0 and dl.max() <= 1e-3
