@@ -27,12 +27,13 @@
 //   * Exponents: one E8M0 byte per block, [BH][Np / 64].
 //
 // The attention kernel is the bf16 forward's design at FP8 rates: a
-// workgroup of 8 waves owns 256 queries (32 per wave) and walks 64-key tiles,
-// double-buffered in LDS through buffer_load ... lds; per tile each wave
-// computes S^T = K Q^T (two 32-key blocks, two K = 64 MFMAs each), the
-// softmax against a lagging reference max, and O^T += V^T P^T (four MFMAs
-// over the tile's 64 keys).  The softmax of tile t runs while the matrix
-// cores compute S of tile t+1 and P V of tile t-1.  P is rounded to E4M3
+// workgroup of 8 waves owns 256 queries (32 per wave) and walks 128-key tiles
+// (two 64-key blocks), double-buffered in LDS through buffer_load ... lds, one
+// barrier per tile; per 64-key block each wave computes S^T = K Q^T (two
+// 32-key halves, two K = 64 MFMAs each), the softmax against a lagging
+// reference max, and O^T += V^T P^T (four MFMAs over the block's 64 keys).
+// The softmax of block s runs while the matrix cores compute S of block s+1
+// and P V of block s-1; K and V are copied two blocks ahead of their use.  P is rounded to E4M3
 // for the product (the reference may lag the row max by at most 8 in log2
 // units, so P <= 256 stays inside E4M3); O is divided by the fp32 sum of the
 // unrounded P, which also gives the LSE.
@@ -56,7 +57,7 @@ constexpr int kRowsBlk = 64;                 // quantization block = K/V tile ro
 constexpr int kWaves = 8;
 constexpr int kThreads = kWave * kWaves;
 constexpr int kBr = 32 * kWaves;             // queries per workgroup
-constexpr int kTileBytes = kRowsBlk * kD;    // one K tile or one V^T tile: 8 KB
+constexpr int kTileBytes = 2 * kRowsBlk * kD;  // one K or V^T tile (128 keys): 16 KB
 constexpr float kRefSlack = 8.f;             // P <= 2^8 inside E4M3's 448
 constexpr int kE8M0One = 127;
 
@@ -173,14 +174,12 @@ __global__ __launch_bounds__(256) void quantize_kernel(const __bf16 *__restrict_
 // ---------------------------------------------------------------------------
 // Attention
 
-// LDS swizzles (16-byte chunk c of row r at chunk position c ^ swz(r)).
-//  K rows are 128 bytes, two per 256-byte bank line; a ds_read_b128 by lanes
-//  0..15 reads rows 0..15 at one chunk: distinct positions need
-//  (r & 1, c ^ swz(r)) distinct, which (r & 7) ^ ((r >> 3) & 1) gives.
-//  V^T rows are 64 bytes, four per bank line: (r & 3, c ^ swz(r)) distinct
-//  over 16 rows needs swz(r) = (r >> 2) & 3.
+// LDS swizzle (16-byte chunk c of row r at chunk position c ^ swz(r)).  K
+// rows and V^T rows of a 128-key tile are both 128 bytes, two per 256-byte
+// bank line; a ds_read_b128 by lanes 0..15 reads rows 0..15 at one chunk:
+// distinct positions need (r & 1, c ^ swz(r)) distinct, which
+// (r & 7) ^ ((r >> 3) & 1) gives.
 __device__ __forceinline__ int swz_k(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-__device__ __forceinline__ int swz_v(int r) { return (r >> 2) & 3; }
 
 struct F8Args {
     const uint8_t *Q, *K, *VT;       // [BH][Np][128], [BH][Np][128], [BH][128][Np]
@@ -226,7 +225,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
     const uint8_t *Kh = a.K + (size_t)bh * Np * kD;
     const uint8_t *Vh = a.VT + (size_t)bh * kD * Np;
-    const uint8_t *keh = a.ke + (size_t)bh * a.nblk, *veh = a.ve + (size_t)bh * a.nblk;
     const __amdgpu_buffer_rsrc_t vrsrc =
         __builtin_amdgcn_make_buffer_rsrc((void *)Vh, (short)0, (int)((uint32_t)kD * (uint32_t)Np), kBufferFlags);
 
@@ -235,50 +233,72 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         if (pass > 0)
             __syncthreads();
         // Per-lane offsets, computed afresh in each pass from an opaque copy of
-        // the lane index so that they are not kept live across passes.  DMA:
-        // wave w copies 1 KB slice w of each tile: K rows 8 w + lane / 8
-        // (chunk lane % 8), V^T rows 16 w + lane / 4 (chunk lane % 4).
+        // the lane index so that they are not kept live across passes.  A tile
+        // holds 128 keys (two 64-key blocks): K as 128 rows of 128 bytes, V^T
+        // as 128 rows (head dim) of 128 bytes (keys).  DMA: wave w copies 1 KB
+        // slices 2 w and 2 w + 1 of each, rows 8 s + lane / 8, chunk lane % 8.
         int lane_p = lane;
         asm volatile("" : "+v"(lane_p));
         const int n = lane_p & 31, half = lane_p >> 5;
-        const int kr = 8 * wave_u + lane_p / 8, kp = lane_p % 8;
-        const uint32_t kdma = (uint32_t)(kr * kD + ((kp ^ swz_k(kr)) << 4));
-        const int vr = 16 * wave_u + lane_p / 4, vp = lane_p % 4;
-        const uint32_t vdma = (uint32_t)(vr * Np + ((vp ^ swz_v(vr)) << 4));
-        // S operand: row n of a 32-key block, bytes 64 st + 32 half .. +31 (chunks
-        // 4 st + 2 half + c).  P V operand: V^T row n of a 32-row block, bytes
-        // 32 half .. +31 of the tile (chunks 2 half + c).
-        uint32_t koff[2][2], voff[2];
+        uint32_t kdma[2], vdma[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int r = 8 * (2 * wave_u + i) + lane_p / 8, pos = lane_p % 8;
+            kdma[i] = (uint32_t)(r * kD + ((pos ^ swz_k(r)) << 4));
+            vdma[i] = (uint32_t)(r * Np + ((pos ^ swz_k(r)) << 4));
+        }
+        // S operand: row n of a 32-key block, bytes 64 st + 32 half .. +31
+        // (chunks 4 st + 2 half + c).  P V operand of block b64 of a tile: V^T
+        // row n of a 32-row block, bytes 64 b64 + 32 half .. +31 (chunks
+        // 4 b64 + 2 half + c).  Both swizzles repeat every 16 rows.
+        uint32_t koff[2][2], voff[2][2];
 #pragma unroll
         for (int st = 0; st < 2; ++st)
 #pragma unroll
-            for (int c = 0; c < 2; ++c)
+            for (int c = 0; c < 2; ++c) {
                 koff[st][c] = (uint32_t)(n * kD + (((4 * st + 2 * half + c) ^ swz_k(n)) << 4));
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-            voff[c] = (uint32_t)(n * kRowsBlk + (((2 * half + c) ^ swz_v(n)) << 4));
+                voff[st][c] = (uint32_t)(n * kD + (((4 * st + 2 * half + c) ^ swz_k(n)) << 4));
+            }
         const int q0 = qt * kBr;
         const int qw0 = q0 + 32 * wave_u;
         const int qidx = qw0 + n;
         const bool q_ok = qidx < N;
         const int kv_end = CAUSAL ? min(N, q0 + kBr) : N;
-        const int t_end = (kv_end + kRowsBlk - 1) / kRowsBlk;
+        const int nb_end = (kv_end + kRowsBlk - 1) / kRowsBlk;  // 64-key blocks
+        const int t_end = (nb_end + 1) / 2;                      // 128-key tiles
         const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
             (void *)Kh, (short)0, (int)((uint32_t)kv_end * (uint32_t)kD), kBufferFlags);
 
+        // Tile t of K (rows past kv_end: zeros, no memory access) and of V^T
+        // (keys 128 t .. +127 of every row; keys past the row belong to no
+        // visible block and are never multiplied by a nonzero P).
         auto load_k = [&](int t, char *buf) __attribute__((always_inline)) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, LDS_PTR(void, buf + wave_u * 1024), 16, kdma,
-                                                     (int)((uint32_t)t * (uint32_t)kTileBytes), 0, 0);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, LDS_PTR(void, buf + (2 * wave_u + i) * 1024), 16,
+                                                         kdma[i], (int)((uint32_t)t * (uint32_t)kTileBytes), 0, 0);
         };
         auto load_v = [&](int t, char *buf) __attribute__((always_inline)) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, LDS_PTR(void, buf + wave_u * 1024), 16, vdma,
-                                                     (int)((uint32_t)t * (uint32_t)kRowsBlk), 0, 0);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, LDS_PTR(void, buf + (2 * wave_u + i) * 1024), 16,
+                                                         vdma[i], (int)((uint32_t)t * (uint32_t)(2 * kRowsBlk)), 0, 0);
+        };
+        // Block exponents by scalar loads of the dword holding the byte (a
+        // dword-aligned read holding an in-range byte stays inside one page);
+        // scalar loads are counted apart from the tile copies, so waiting for
+        // one never waits for the other.
+        auto exp_of = [&](const uint8_t *base, int blk) __attribute__((always_inline)) {
+            const size_t g = (size_t)bh * a.nblk + (size_t)min(blk, a.nblk - 1);
+            const uint32_t word = ((const __attribute__((address_space(4))) uint32_t *)base)[g >> 2];
+            return (int)((word >> (8 * (g & 3))) & 0xffu);
         };
 
         load_k(0, sk0);
-        load_k(1, sk1);  // past kv_end: zeros, no memory access
-        // V buffer 1 is multiplied by the zero P of "tile -1" in the first step:
-        // it must hold finite values.
+        load_k(1, sk1);
+        load_v(0, sv0);
+        // V buffer 1 is multiplied by the zero P of "block -1" in the first
+        // step: it must hold finite values.
 #pragma unroll
         for (int i = 0; i < kTileBytes / (16 * kThreads); ++i)
             *LDS_PTR(u32x4, sv1 + 16 * (tid + i * kThreads)) = u32x4{};
@@ -297,27 +317,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             }
         }
         const int qs = qw0 < N ? (int)a.qe[(size_t)bh * a.nblk + qw0 / kRowsBlk] : kE8M0One;
-        const int ks0 = keh[0], ks1 = keh[min(1, a.nblk - 1)];
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
 
-        // Scores of the 64-key tile t (two 32-key blocks) from K buffer kb.
-        auto scores = [&](const char *kbuf, int ks, f32x16 *s) __attribute__((always_inline)) {
+        // Scores of 64-key block b64 of the tile in K buffer kbuf.
+        auto scores = [&](const char *kbuf, int b64, int ks, f32x16 *s) __attribute__((always_inline)) {
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
                 s[b] = f32x16{};
 #pragma unroll
                 for (int st = 0; st < 2; ++st)
-                    s[b] = mfma8(lds_pair(kbuf + b * 32 * kD + koff[st][0], kbuf + b * 32 * kD + koff[st][1]),
+                    s[b] = mfma8(lds_pair(kbuf + (64 * b64 + 32 * b) * kD + koff[st][0],
+                                          kbuf + (64 * b64 + 32 * b) * kD + koff[st][1]),
                                  qop[st], s[b], ks, qs);
             }
         };
         f32x16 sc[2];
-        scores(sk0, ks0, sc);
+        scores(sk0, 0, exp_of(a.ke, 0), sc);
 
-        // Register 4 j + e of block b holds key 64 t + 32 b + 8 j + 4 half + e.
-        auto visible = [&](int t, int b, int r) __attribute__((always_inline)) {
-            const int key = 64 * t + 32 * b + 8 * (r >> 2) + 4 * half + (r & 3);
+        // Register 4 j + e of 32-key half b holds key 64 s + 32 b + 8 j + 4 half + e
+        // of 64-key block s.
+        auto visible = [&](int blk, int b, int r) __attribute__((always_inline)) {
+            const int key = 64 * blk + 32 * b + 8 * (r >> 2) + 4 * half + (r & 3);
             return key < N && (!CAUSAL || key <= qidx);
         };
         float m_ref, m_sub, m_thr;
@@ -343,41 +364,46 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         bool pending = false;
         float alpha_pend = 1.f;
         i32x8 pb_prev = i32x8{};
-        int ks = ks1, vs = kE8M0One;  // exponents of K tile 1 and of "V tile -1"
 
-        // One 64-key step (tile t, K buffer P = t % 2).  MASKED: tile t needs
-        // the causal / sequence-end mask; NEXT_MASKED: tile t+1 does (past
-        // the last tile every key is invisible, so the last step takes it
-        // too).  ks: exponent of K tile t+1; vs: of V tile t-1.  Both were
-        // loaded in the previous step, so nothing in a step waits on memory
-        // but its opening barrier.
-        auto step = [&](int t, auto parity_tag, auto masked_tag, auto next_masked_tag) __attribute__((always_inline)) {
+        // One 64-key step: block s = 2 t + J of tile t (K buffer P = t % 2).
+        // The softmax of block s interleaves with the scores of block s+1 and
+        // P V of block s-1:
+        //   J = 0: scores of block 2t+1 (tile t, K buffer P, rows 64..127),
+        //          P V of block 2t-1 (tile t-1, V buffer 1-P, keys 64..127);
+        //   J = 1: scores of block 2t+2 (tile t+1, K buffer 1-P, rows 0..63),
+        //          P V of block 2t (tile t, V buffer P, keys 0..63), and the
+        //          copies of K tile t+2 into K buffer P and V tile t+1 into V
+        //          buffer 1-P (both released before the tile's barrier).
+        // MASKED: block s needs the causal / sequence-end mask; NEXT_MASKED:
+        // block s+1 does (past the last block every key is invisible).
+        auto step = [&](int t, auto parity_tag, auto half_tag, auto masked_tag, auto next_masked_tag)
+            __attribute__((always_inline)) {
             constexpr int P = decltype(parity_tag)::value;
+            constexpr int J = decltype(half_tag)::value;
             constexpr bool MASKED = decltype(masked_tag)::value;
             constexpr bool NEXT_MASKED = decltype(next_masked_tag)::value;
-            char *kcur = P ? sk1 : sk0;   // K tile t (already consumed into sc)
-            char *knext = P ? sk0 : sk1;  // K tile t+1
-            char *vprev = P ? sv0 : sv1;  // V tile t-1
-            char *vcur = P ? sv1 : sv0;   // V tile t, loaded now
-            // Tile t+1's K and tile t-1's V have landed, and every wave is done
-            // with K tile t and V tile t-2, whose buffers are refilled now.
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            load_k(t + 2, kcur);  // past kv_end: zeros, no memory access
-            load_v(t, vcur);
-            const int ks_pf = keh[min(t + 2, a.nblk - 1)], vs_pf = veh[t];
+            char *kown = P ? sk1 : sk0, *kother = P ? sk0 : sk1;
+            char *vown = P ? sv1 : sv0, *vother = P ? sv0 : sv1;
+            const char *knext = J == 0 ? kown : kother;
+            const char *vprev = J == 0 ? vother : vown;
+            constexpr int knext_b64 = J == 0 ? 1 : 0, vprev_b64 = J == 0 ? 1 : 0;
+            const int blk = 2 * t + J;
+            if constexpr (J == 1) {
+                load_k(t + 2, kown);
+                load_v(t + 1, vother);
+            }
+            const int ks = exp_of(a.ke, blk + 1), vs = blk > 0 ? exp_of(a.ve, blk - 1) : kE8M0One;
             // Keep the LDS offsets opaque (so they ride in the ds_read offset
             // field instead of being hoisted as per-buffer sums) and the
             // softmax inside its step.
 #pragma unroll
             for (int st = 0; st < 2; ++st)
-                asm volatile("" : "+v"(koff[st][0]), "+v"(koff[st][1]));
-            asm volatile("" : "+v"(voff[0]), "+v"(voff[1]));
+                asm volatile("" : "+v"(koff[st][0]), "+v"(koff[st][1]), "+v"(voff[st][0]), "+v"(voff[st][1]));
             asm volatile("" : "+v"(sc[0]), "+v"(sc[1]));
 
-            // P of tile t against the reference, rounded to E4M3 in the order
+            // P of block s against the reference, rounded to E4M3 in the order
             // of the P V operand: byte 4 w + i is register 4 (w & 3) + i of
-            // block w >> 2.
+            // 32-key half w >> 2.
             float p[2][16];
 #pragma unroll
             for (int b = 0; b < 2; ++b)
@@ -385,7 +411,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 for (int r = 0; r < 16; ++r) {
                     p[b][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[b][r], c_log2, -m_sub));
                     if constexpr (MASKED)
-                        p[b][r] = visible(t, b, r) ? p[b][r] : 0.f;
+                        p[b][r] = visible(blk, b, r) ? p[b][r] : 0.f;
                 }
             float rs0 = p[0][0], rs1 = p[0][1];
 #pragma unroll
@@ -402,13 +428,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 pb[w] = __builtin_amdgcn_cvt_pk_fp8_f32(pp[2], pp[3], u, true);
             }
 
-            // Scores of tile t+1 (past the end: zero rows, discarded) and P V
-            // of tile t-1.
             f32x16 sn[2];
-            scores(knext, ks, sn);
+            scores(knext, knext_b64, ks, sn);
 #pragma unroll
             for (int db = 0; db < 4; ++db)
-                oacc[db] = mfma8(lds_pair(vprev + db * 32 * kRowsBlk + voff[0], vprev + db * 32 * kRowsBlk + voff[1]),
+                oacc[db] = mfma8(lds_pair(vprev + db * 32 * kD + voff[vprev_b64][0],
+                                          vprev + db * 32 * kD + voff[vprev_b64][1]),
                                  pb_prev, oacc[db], vs, kE8M0One);
 
             float mx;
@@ -418,7 +443,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 for (int b = 0; b < 2; ++b)
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
-                        mx = fmaxf(mx, visible(t + 1, b, r) ? sn[b][r] * c_log2 : kNegInf);
+                        mx = fmaxf(mx, visible(blk + 1, b, r) ? sn[b][r] * c_log2 : kNegInf);
             } else {  // every key visible and c_log2 > 0
                 float m0 = sn[0][0];
 #pragma unroll
@@ -454,47 +479,56 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             sc[0] = sn[0];
             sc[1] = sn[1];
             pb_prev = pb;
-            ks = ks_pf;
-            vs = vs_pf;
+        };
+        // One 128-key tile: block 2t, the barrier (K tile t+1 and V tile t have
+        // landed; every wave is done with K tile t and V tile t-1), block 2t+1.
+        auto tile = [&](int t, auto parity_tag, auto masked_tag, auto mid_masked_tag, auto next_masked_tag)
+            __attribute__((always_inline)) {
+            step(t, parity_tag, std::integral_constant<int, 0>{}, masked_tag, mid_masked_tag);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            step(t, parity_tag, std::integral_constant<int, 1>{}, mid_masked_tag, next_masked_tag);
         };
         using P0 = std::integral_constant<int, 0>;
         using P1 = std::integral_constant<int, 1>;
         using Unmasked = std::false_type;
         using Masked = std::true_type;
-        // Tiles [0, t_free) need no mask: inside the sequence and at or below
+        // Blocks [0, b_free) need no mask: inside the sequence and at or below
         // the causal diagonal of every query of the workgroup (and a positive
-        // scale, which the unmasked row max assumes).  t_free is made even so
-        // that the loops walk (buffer 0, buffer 1) pairs; the last unmasked
-        // pair is peeled because the tile after it needs the mask.
-        int t_free = N / kRowsBlk;
+        // scale, which the unmasked row max assumes).  Whole unmasked tile
+        // pairs run in the first loop; the last one is peeled because the block
+        // after it needs the mask.
+        int b_free = N / kRowsBlk;
         if (CAUSAL)
-            t_free = min(t_free, (q0 + 1) / kRowsBlk);
+            b_free = min(b_free, (q0 + 1) / kRowsBlk);
         if (!(c_log2 > 0.f))
-            t_free = 0;
-        t_free = min(t_free, t_end) & ~1;
+            b_free = 0;
+        b_free = min(b_free, nb_end);
+        const int t_free = (b_free / 2) & ~1;  // unmasked tiles, an even count
         int t = 0;
         for (; t + 2 < t_free; t += 2) {
-            step(t, P0{}, Unmasked{}, Unmasked{});
-            step(t + 1, P1{}, Unmasked{}, Unmasked{});
+            tile(t, P0{}, Unmasked{}, Unmasked{}, Unmasked{});
+            tile(t + 1, P1{}, Unmasked{}, Unmasked{}, Unmasked{});
         }
         if (t < t_free) {
-            step(t, P0{}, Unmasked{}, Unmasked{});
-            step(t + 1, P1{}, Unmasked{}, Masked{});
+            tile(t, P0{}, Unmasked{}, Unmasked{}, Unmasked{});
+            tile(t + 1, P1{}, Unmasked{}, Unmasked{}, Masked{});
             t += 2;
         }
         for (; t < t_end; t += 2) {
-            step(t, P0{}, Masked{}, Masked{});
+            tile(t, P0{}, Masked{}, Masked{}, Masked{});
             if (t + 1 < t_end)
-                step(t + 1, P1{}, Masked{}, Masked{});
+                tile(t + 1, P1{}, Masked{}, Masked{}, Masked{});
         }
-        // P V of the last tile.
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        // P V of the last block, 2 t_end - 1 (second half of the last tile,
+        // whose V landed at that tile's barrier); then drain the copies still
+        // in flight before the next pass reuses the buffers.
         {
             char *vlast = ((t_end - 1) & 1) ? sv1 : sv0;
+            const int vs = exp_of(a.ve, 2 * t_end - 1);
 #pragma unroll
             for (int db = 0; db < 4; ++db)
-                oacc[db] = mfma8(lds_pair(vlast + db * 32 * kRowsBlk + voff[0], vlast + db * 32 * kRowsBlk + voff[1]),
+                oacc[db] = mfma8(lds_pair(vlast + db * 32 * kD + voff[1][0], vlast + db * 32 * kD + voff[1][1]),
                                  pb_prev, oacc[db], vs, kE8M0One);
             if (pending) {
 #pragma unroll
@@ -502,6 +536,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                     oacc[b] *= alpha_pend;
             }
         }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
 
         const float l_tot = wave_half_sum(l_run);
         if (q_ok) {
