@@ -283,11 +283,10 @@ __global__ __launch_bounds__(Shape<D>::kThreads) __attribute__((amdgpu_waves_per
     __shared__ __attribute__((aligned(1024))) char sv0[S::kBytes];
     __shared__ __attribute__((aligned(1024))) char sv1[S::kBytes];
 
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int wave_u = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int n = lane & 31, half = lane >> 5;
     const int N = a.N, nblk = a.ntiles;
-    Offsets<D> off(wave, lane);
 
     const int n_units = CAUSAL ? (nblk + 1) / 2 : nblk;
     int bh, unit;
@@ -297,6 +296,11 @@ __global__ __launch_bounds__(Shape<D>::kThreads) __attribute__((amdgpu_waves_per
     const __bf16 *Kh = a.K + head, *Vh = a.V + head;
 
     for (int pass = 0; pass < npass; ++pass) {
+        // Per-lane LDS offsets, built afresh in each pass from an opaque copy of
+        // the lane index so that they are not held live across passes.
+        int lane_p = lane;
+        asm volatile("" : "+v"(lane_p));
+        Offsets<D> off(wave_u, lane_p);
         if (pass > 0)
             __syncthreads();  // every wave is done with the previous block's LDS
         const int q0 = pair_block(CAUSAL, nblk, unit, pass) * S::kBlock;
@@ -420,11 +424,10 @@ __global__ __launch_bounds__(Shape<D>::kThreads) __attribute__((amdgpu_waves_per
     __shared__ __attribute__((aligned(1024))) char sg1[S::kBytes];
     __shared__ __attribute__((aligned(256))) float sl0[kTile], sl1[kTile], sd0[kTile], sd1[kTile];
 
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int wave_u = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int n = lane & 31, half = lane >> 5;
     const int N = a.N, nblk = a.ntiles;
-    Offsets<D> off(wave, lane);
 
     const int n_units = CAUSAL ? (nblk + 1) / 2 : nblk;
     int bh, unit;
@@ -434,17 +437,21 @@ __global__ __launch_bounds__(Shape<D>::kThreads) __attribute__((amdgpu_waves_per
     const __bf16 *Qh = a.Q + head, *Gh = a.dO + head;
     const float *L2h = a.L2 + (size_t)bh * N, *Dh = a.Dsum + (size_t)bh * N;
 
-    // One query tile (Q, dO, L2, D) into buffer set `second`.
-    auto load_all = [&](int t, bool second) __attribute__((always_inline)) {
-        load_tile<D>(Qh, N, t * kTile, second ? sq1 : sq0, wave_u, off.dma);
-        load_tile<D>(Gh, N, t * kTile, second ? sg1 : sg0, wave_u, off.dma);
-        if (wave_u == 0)
-            load_vec(L2h, N, t * kTile, second ? sl1 : sl0, lane);
-        else if (wave_u == 1)
-            load_vec(Dh, N, t * kTile, second ? sd1 : sd0, lane);
-    };
-
     for (int pass = 0; pass < npass; ++pass) {
+        // Per-lane LDS offsets, built afresh in each pass from an opaque copy of
+        // the lane index so that they are not held live across passes.
+        int lane_p = lane;
+        asm volatile("" : "+v"(lane_p));
+        Offsets<D> off(wave_u, lane_p);
+        // One query tile (Q, dO, L2, D) into buffer set `second`.
+        auto load_all = [&](int t, bool second) __attribute__((always_inline)) {
+            load_tile<D>(Qh, N, t * kTile, second ? sq1 : sq0, wave_u, off.dma);
+            load_tile<D>(Gh, N, t * kTile, second ? sg1 : sg0, wave_u, off.dma);
+            if (wave_u == 0)
+                load_vec(L2h, N, t * kTile, second ? sl1 : sl0, lane);
+            else if (wave_u == 1)
+                load_vec(Dh, N, t * kTile, second ? sd1 : sd0, lane);
+        };
         if (pass > 0)
             __syncthreads();
         const int k0 = pair_block(CAUSAL, nblk, unit, pass) * S::kBlock;
