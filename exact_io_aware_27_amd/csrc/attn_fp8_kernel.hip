@@ -57,8 +57,8 @@ constexpr int kRowsBlk = 64;                 // quantization block = K/V tile ro
 constexpr int kWaves = 8;
 constexpr int kThreads = kWave * kWaves;
 constexpr int kBr = 32 * kWaves;             // queries per workgroup
-constexpr int kTileBytes = 2 * kRowsBlk * kD;  // one K or V^T tile (128 keys): 16 KB
-constexpr float kRefSlack = 8.f;             // P <= 2^8 inside E4M3's 448
+[[maybe_unused]] constexpr int kTileBytes = 2 * kRowsBlk * kD;  // one K or V^T tile (128 keys): 16 KB
+[[maybe_unused]] constexpr float kRefSlack = 8.f;  // P <= 2^8 inside E4M3's 448
 constexpr int kE8M0One = 127;
 
 // ---------------------------------------------------------------------------

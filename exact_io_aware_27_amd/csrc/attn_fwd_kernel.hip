@@ -78,7 +78,7 @@ constexpr int kBc = 64;      // keys per K/V tile (two 32-key blocks)
 // A block's probabilities are taken against a reference max that may lag
 // the true running max by up to kRefSlack (log2 units): p <= 2^16.  A row
 // whose next block would exceed that moves the reference to its exact max.
-constexpr float kRefSlack = 16.f;
+[[maybe_unused]] constexpr float kRefSlack = 16.f;
 
 // Workgroup shape per head dim.  d = 128: 8 waves (256 queries), one
 // workgroup per CU, two waves per SIMD from the same workgroup: each K/V
