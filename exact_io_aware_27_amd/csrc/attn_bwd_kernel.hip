@@ -25,13 +25,15 @@
 //
 // gfx950 mapping (shared by both kernels)
 //   * 32 rows (queries or keys) per wave; 8 waves per workgroup for d = 128
-//     (one per CU), 4 for d = 64 (two per CU).  Each lane owns one row of its wave (lane % 32) in
-//     the 32x32 accumulator layout of v_mfma_f32_32x32x16_bf16 and 16 of the
-//     32 columns of the other side.
+//     (one workgroup per CU), 4 for d = 64 (two per CU).  Each lane owns one
+//     row of its wave (lane % 32) in the 32x32 accumulator layout of
+//     v_mfma_f32_32x32x16_bf16 and 16 of the 32 columns of the other side.
 //   * The operands walked by the loop (K and V in the dQ kernel, Q and dO in
 //     the dK/dV kernel) go from global memory to LDS in 64-row tiles with
-//     buffer_load_dwordx4 ... lds, double-buffered, one barrier per tile.
-//     Rows past N read as zeros, with no memory access.
+//     buffer_load_dwordx4 ... lds, double-buffered, one barrier per tile;
+//     tiles are walked in (buffer 0, buffer 1) pairs so that every LDS
+//     address is a constant plus a per-lane offset.  Rows past N read as
+//     zeros, with no memory access.
 //   * Each tile is read both row-wise (ds_read_b128, as the A operand of a
 //     product over the head dim) and transposed (ds_read_b64_tr_b16, as the
 //     A operand of a product over the rows), so one XOR swizzle of 16-byte
