@@ -147,6 +147,17 @@ def make_qkv_outliers(B, H, N, d, seed, frac=1e-3, outlier_sigma=10.0):
     return tuple(out)
 
 
+def make_kv_on_device(B, H, Nk, d, seed, device):
+    """K and V [B, H, Nk, d] drawn on `device` (standard normal, bfloat16) by a
+    seeded generator there: for the largest key counts, whose fp32 draws on
+    the host would take minutes and tens of GB."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    k = torch.randn((B, H, Nk, d), generator=g, device=device, dtype=torch.bfloat16)
+    v = torch.randn((B, H, Nk, d), generator=g, device=device, dtype=torch.bfloat16)
+    return k, v
+
+
 def make_qkv(B, H, N, d, seed, sigma_qk=1.0, sigma_v=1.0):
     """Q, K, V as CPU bfloat16 tensors [B, H, N, d], drawn in that order."""
     g = torch.Generator(device="cpu")

@@ -139,3 +139,24 @@ def test_every_output_element_is_written_with_splits():
                           torch.cuda.current_stream())
     torch.cuda.synchronize()
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_largest_key_count_the_interface_admits(causal):
+    """Nk * d just below 2^31 (Nk = 16777215 keys, d = 128: 4.3 GB each for K
+    and V): the byte offsets inside a head reach 2^32 - 512, the edge of the
+    kernels' unsigned 32-bit range.  Two queries (the last two positions)
+    against every key, in 64 ranges, checked against the oracle."""
+    B, H, Nq, d = 1, 1, 2, 128
+    Nk = (1 << 31) // d - 1
+    say("case: largest key count", (B, H, Nq, Nk, d), "causal" if causal else "non-causal")
+    k, v = inputs.make_kv_on_device(B, H, Nk, d, seed=5100 + causal, device=DEV)
+    q = inputs.make_qkv(B, H, Nq, d, seed=5102)[0]
+    scale = 1.0 / math.sqrt(d)
+    from exact_io_aware_27_amd import attn
+    o, lse = attn.attention_splitkv(q.to(DEV), k, v, 64, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention(q, k.cpu(), v.cpu(), causal, scale)
+    rep = parity.compare(o, lse, o_ref, lse_ref)
+    say("  ", rep)
+    parity.assert_parity(rep, "largest key count")
