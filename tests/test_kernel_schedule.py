@@ -64,3 +64,36 @@ def test_steps_interleave_mfma_with_softmax(asm, instance):
             h, first, " ".join(instrs[:first + 1]))
         checked += 1
     assert checked >= 2, "expected the unmasked and the masked step loops"
+
+
+@pytest.mark.parametrize("instance", INSTANCES)
+def test_no_scratch_in_key_loops(asm, instance):
+    """No spill or reload runs inside a key loop.  Every basic block's label
+    carries the compiler's loop annotation (the loop header it belongs to);
+    the key loops are the innermost loops that issue MFMAs, and none of their
+    blocks may touch scratch."""
+    body = _instance(asm, instance)
+    loop_of = []  # per line: header label of the innermost loop holding the line, or None
+    parent = {}   # loop header -> enclosing loop header
+    cur = None
+    for i, l in enumerate(body):
+        m = re.match(r"^(?:\.L(BB\w+)|; %bb\.(\d+)):", l)  # a labelled or a fall-through block
+        if m:
+            note = l + (body[i + 1] if i + 1 < len(body) else "")
+            if "Loop Header" in note and m.group(1):
+                cur = m.group(1)
+                up = re.findall(r"Parent Loop (BB\w+)", note)
+                parent.setdefault(cur, up[-1] if up else None)
+            else:
+                inner = re.search(r"in Loop: Header=(BB\w+)", l)
+                cur = inner.group(1) if inner else None
+        loop_of.append(cur)
+    has_child = {p for p in parent.values() if p}
+    mfma = {}
+    for l, lp in zip(body, loop_of):
+        if lp and "v_mfma" in l:
+            mfma[lp] = mfma.get(lp, 0) + 1
+    key_loops = {lp for lp, n in mfma.items() if n >= 4 and lp not in has_child}
+    assert len(key_loops) >= 2, "expected the unmasked and the masked key loops, found %s" % sorted(key_loops)
+    spills = [(lp, l.strip()) for l, lp in zip(body, loop_of) if lp in key_loops and "scratch_" in l]
+    assert not spills, "scratch access inside a key loop: %s" % spills[:3]
