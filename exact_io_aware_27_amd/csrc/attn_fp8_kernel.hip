@@ -76,25 +76,71 @@ __device__ __forceinline__ int block_exp(float amax)
     return max(-127, min(127, E));
 }
 
-// One 64-row block of one head per workgroup (256 threads): thread t owns
-// columns 8 (t % 16) .. +7 of rows 16 p + t / 16, p = 0..3.  ROTATE applies
+// DPP moves within rows of 16 lanes (no LDS traffic): quad_perm, and
+// row_ror n, where lane i reads lane (i - n) mod 16 of its row.  BANKS
+// selects the groups of 4 lanes written; mov leaves the others undefined,
+// update keeps them from `old`.
+template <int CTRL, int BANKS>
+__device__ __forceinline__ float dpp_mov(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, BANKS, false));
+}
+
+template <int CTRL, int BANKS>
+__device__ __forceinline__ float dpp_update(float old, float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                                 __builtin_bit_cast(int, x), CTRL, 0xf, BANKS, false));
+}
+
+// One butterfly stage across the 16 lanes of a row: lane c pairs with lane
+// c ^ m; the lower lane of a pair keeps a + b, the upper one a - b (a the
+// lower lane's value).  fma(+-1, v, o) rounds exactly as v + o and o - v.
+template <int M>
+__device__ __forceinline__ float row_butterfly(float v, float sign)
+{
+    float o;
+    if constexpr (M == 1)
+        o = dpp_mov<0xB1, 0xf>(v);  // quad_perm [1, 0, 3, 2]
+    else if constexpr (M == 2)
+        o = dpp_mov<0x4E, 0xf>(v);  // quad_perm [2, 3, 0, 1]
+    else if constexpr (M == 8)
+        o = dpp_mov<0x128, 0xf>(v);  // row_ror 8
+    else {  // M == 4: lanes 0-3 and 8-11 read 4 ahead, lanes 4-7 and 12-15 4 behind
+        o = dpp_mov<0x12C, 0x5>(v);        // row_ror 12 (lane i reads i - 12 = i + 4) into banks 0, 2
+        o = dpp_update<0x124, 0xa>(o, v);  // row_ror 4 (lane i reads i - 4) into banks 1, 3
+    }
+    return __builtin_fmaf(sign, v, o);
+}
+
+// One 64-row block of one head per workgroup (256 threads); thread t owns
+// columns 8 (t % 16) .. +7 of four rows: rows 16 p + t / 16 (p = 0..3), or,
+// for the transposed V, the consecutive rows 4 (t / 16) + p.  ROTATE applies
 // the signs and the fast Hadamard transform (three stages inside a thread,
-// four across the 16 threads of a row); TRANSPOSE writes V^T in the tile's
-// key order through LDS.
+// four across the 16 lanes of a row, through DPP moves); TRANSPOSE converts
+// column by column (the four rows of one column are four consecutive bytes of
+// the tile's key order) and writes V^T through LDS.
 template <bool ROTATE, bool TRANSPOSE>
 __global__ __launch_bounds__(256) void quantize_kernel(const __bf16 *__restrict__ x, uint8_t *__restrict__ out,
                                                        uint8_t *__restrict__ exps, int N, int Np, int nblk,
                                                        uint32_t s0, uint32_t s1, uint32_t s2, uint32_t s3)
 {
     __shared__ float wmax[4];
+    // V^T staging: column c's 64 key bytes at 64 c, 16-byte chunk q of it at
+    // chunk q ^ ((c >> 3) & 3), which spreads a column-wise write over banks.
     __shared__ __attribute__((aligned(16))) uint8_t tr[TRANSPOSE ? kD * kRowsBlk : 16];
     const int bh = blockIdx.x / nblk, blk = blockIdx.x % nblk;
     const int t = threadIdx.x, c16 = t & 15, rsub = t >> 4;
+    auto row_of = [&](int p) { return TRANSPOSE ? 4 * rsub + p : 16 * p + rsub; };
+    float sgn[4];  // +1 for the lower lane of a stage-m pair, -1 for the upper
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        sgn[i] = (c16 >> i) & 1 ? -1.f : 1.f;
     float v[4][8];
     float amax = 0.f;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        const int row = blk * kRowsBlk + 16 * p + rsub;
+        const int row = blk * kRowsBlk + row_of(p);
         bf16x8 in = bf16x8{};
         if (row < N)
             in = *reinterpret_cast<const bf16x8 *>(x + ((size_t)bh * N + row) * kD + 8 * c16);
@@ -118,12 +164,12 @@ __global__ __launch_bounds__(256) void quantize_kernel(const __bf16 *__restrict_
                         v[p][i + h] = a - b;
                     }
 #pragma unroll
-            for (int m = 1; m < 16; m *= 2)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float o = __shfl_xor(v[p][e], m, 16);
-                    v[p][e] = (c16 & m) ? o - v[p][e] : v[p][e] + o;
-                }
+            for (int e = 0; e < 8; ++e) {
+                v[p][e] = row_butterfly<1>(v[p][e], sgn[0]);
+                v[p][e] = row_butterfly<2>(v[p][e], sgn[1]);
+                v[p][e] = row_butterfly<4>(v[p][e], sgn[2]);
+                v[p][e] = row_butterfly<8>(v[p][e], sgn[3]);
+            }
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e)
@@ -137,34 +183,34 @@ __global__ __launch_bounds__(256) void quantize_kernel(const __bf16 *__restrict_
     __syncthreads();
     amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
     const int E = block_exp(amax);
+    auto fp8x4 = [&](float a, float b, float c, float d) {  // E4M3 bytes of (a, b, c, d) / 2^E, a lowest
+        int u = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(a, -E), __builtin_amdgcn_ldexpf(b, -E), 0,
+                                                false);
+        u = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(c, -E), __builtin_amdgcn_ldexpf(d, -E), u, true);
+        return (uint32_t)u;
+    };
+    if constexpr (!TRANSPOSE) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        uint32_t w[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            int u = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(v[p][4 * h + 0], -E),
-                                                    __builtin_amdgcn_ldexpf(v[p][4 * h + 1], -E), 0, false);
-            u = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(v[p][4 * h + 2], -E),
-                                                __builtin_amdgcn_ldexpf(v[p][4 * h + 3], -E), u, true);
-            w[h] = (uint32_t)u;
+        for (int p = 0; p < 4; ++p) {
+            const u32x2 w = {fp8x4(v[p][0], v[p][1], v[p][2], v[p][3]), fp8x4(v[p][4], v[p][5], v[p][6], v[p][7])};
+            *reinterpret_cast<u32x2 *>(out + ((size_t)bh * Np + blk * kRowsBlk + row_of(p)) * kD + 8 * c16) = w;
         }
-        const int r = 16 * p + rsub;  // row in the block
-        if constexpr (!TRANSPOSE) {
-            *reinterpret_cast<u32x2 *>(out + ((size_t)bh * Np + blk * kRowsBlk + r) * kD + 8 * c16) = u32x2{w[0], w[1]};
-        } else {
-            const int pos = 32 * ((r >> 2) & 1) + 16 * (r >> 5) + 4 * ((r >> 3) & 3) + (r & 3);
+    } else {
+        // rows 4 rsub + p sit at key positions base + p
+        const int base = 32 * (rsub & 1) + 16 * (rsub >> 3) + 4 * ((rsub >> 1) & 3);
+        const int chunk = base >> 4, within = base & 15;
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                tr[(8 * c16 + e) * kRowsBlk + pos] = (uint8_t)(w[e >> 2] >> (8 * (e & 3)));
+        for (int e = 0; e < 8; ++e) {
+            const int col = 8 * c16 + e;
+            *reinterpret_cast<uint32_t *>(tr + col * kRowsBlk + 16 * (chunk ^ (c16 & 3)) + within) =
+                fp8x4(v[0][e], v[1][e], v[2][e], v[3][e]);
         }
-    }
-    if constexpr (TRANSPOSE) {
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int chunk = t + 256 * i, row = chunk >> 2, part = chunk & 3;
-            *reinterpret_cast<u32x4 *>(out + ((size_t)bh * kD + row) * Np + blk * kRowsBlk + 16 * part) =
-                *reinterpret_cast<const u32x4 *>(tr + row * kRowsBlk + 16 * part);
+            const int ch = t + 256 * i, col = ch >> 2, part = ch & 3;
+            *reinterpret_cast<u32x4 *>(out + ((size_t)bh * kD + col) * Np + blk * kRowsBlk + 16 * part) =
+                *reinterpret_cast<const u32x4 *>(tr + col * kRowsBlk + 16 * (part ^ ((col >> 3) & 3)));
         }
     }
     if (t == 0)
