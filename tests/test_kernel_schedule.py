@@ -1,4 +1,5 @@
-"""The compiled step schedule of every kernel instance (CPU only).
+"""The compiled step schedule of every kernel instance, and spill-free key
+loops in every attention kernel (CPU only).
 
 Each 32-key step of attn_fwd_kernel is meant to
 interleave its 16 MFMAs with the softmax VALU work and the LDS operand reads
@@ -66,13 +67,11 @@ def test_steps_interleave_mfma_with_softmax(asm, instance):
     assert checked >= 2, "expected the unmasked and the masked step loops"
 
 
-@pytest.mark.parametrize("instance", INSTANCES)
-def test_no_scratch_in_key_loops(asm, instance):
-    """No spill or reload runs inside a key loop.  Every basic block's label
-    carries the compiler's loop annotation (the loop header it belongs to);
-    the key loops are the innermost loops that issue MFMAs, and none of their
-    blocks may touch scratch."""
-    body = _instance(asm, instance)
+def key_loop_spills(body):
+    """(key loops, scratch accesses inside them) of one kernel's assembly.
+    Every basic block's label carries the compiler's loop annotation (the
+    loop header it belongs to); the key loops are the innermost loops that
+    issue MFMAs."""
     loop_of = []  # per line: header label of the innermost loop holding the line, or None
     parent = {}   # loop header -> enclosing loop header
     cur = None
@@ -94,6 +93,46 @@ def test_no_scratch_in_key_loops(asm, instance):
         if lp and "v_mfma" in l:
             mfma[lp] = mfma.get(lp, 0) + 1
     key_loops = {lp for lp, n in mfma.items() if n >= 4 and lp not in has_child}
-    assert len(key_loops) >= 2, "expected the unmasked and the masked key loops, found %s" % sorted(key_loops)
     spills = [(lp, l.strip()) for l, lp in zip(body, loop_of) if lp in key_loops and "scratch_" in l]
+    return key_loops, spills
+
+
+@pytest.mark.parametrize("instance", INSTANCES)
+def test_no_scratch_in_key_loops(asm, instance):
+    """No spill or reload runs inside a key loop of the forward kernel."""
+    key_loops, spills = key_loop_spills(_instance(asm, instance))
+    assert len(key_loops) >= 2, "expected the unmasked and the masked key loops, found %s" % sorted(key_loops)
     assert not spills, "scratch access inside a key loop: %s" % spills[:3]
+
+
+OTHER_SOURCES = {"bwd": "attn_bwd_kernel.hip", "fp8": "attn_fp8_kernel.hip"}
+
+
+@pytest.fixture(scope="module")
+def other_asm(tmp_path_factory):
+    hipcc = build.HIPCC
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    flags = [f for f in build.FLAGS if f not in ("-shared", "-fPIC") and not f.startswith("-Wl,")]
+    out = {}
+    for key, name in OTHER_SOURCES.items():
+        path = str(tmp_path_factory.mktemp("asm_" + key) / "kernel.s")
+        subprocess.check_call([hipcc] + flags + ["--cuda-device-only", "-S", "-o", path,
+                                                 os.path.join(ROOT, "exact_io_aware_27_amd", "csrc", name)])
+        with open(path) as f:
+            out[key] = f.read().splitlines()
+    return out
+
+
+@pytest.mark.parametrize("key", sorted(OTHER_SOURCES))
+def test_no_scratch_in_backward_and_fp8_key_loops(other_asm, key):
+    """The backward kernels and the FP8 attention kernel: every instance has
+    a key loop and none of its key loops touches scratch."""
+    lines = other_asm[key]
+    names = [l.split(":")[0] for l in lines if re.match(r"^_ZN\w+:", l)]
+    names = [n for n in names if "quantize" not in n]  # no key loop
+    assert len(names) == (8 if key == "bwd" else 2), names
+    for name in names:
+        key_loops, spills = key_loop_spills(_instance(lines, name))
+        assert key_loops, "%s: no key loop found" % name
+        assert not spills, "%s: scratch access inside a key loop: %s" % (name, spills[:3])
