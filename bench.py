@@ -389,7 +389,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="long_causal",
                     help="name of a workload in exact_io_aware_27_amd.inputs.WORKLOADS")
     ap.add_argument("--cpu-rows", type=int, default=1024,
