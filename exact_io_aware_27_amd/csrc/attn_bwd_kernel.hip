@@ -346,9 +346,11 @@ __global__ __launch_bounds__(Shape<D>::kThreads) __attribute__((amdgpu_waves_per
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         // One 64-key tile t in buffer set P = t % 2 (compile-time, so that the
-        // buffer addresses fold into the LDS read offsets).
-        auto tile = [&](int t, auto parity_tag) __attribute__((always_inline)) {
+        // buffer addresses fold into the LDS read offsets).  MASKED tiles may
+        // hold keys after some query of the workgroup; the others need no mask.
+        auto tile = [&](int t, auto parity_tag, auto masked_tag) __attribute__((always_inline)) {
             constexpr int P = decltype(parity_tag)::value;
+            constexpr bool MASKED = decltype(masked_tag)::value;
             char *kc = P ? sk1 : sk0, *vc = P ? sv1 : sv0;
             off.opaque();
             if (t + 1 < t_end) {  // the other buffers were released by the last barrier
@@ -368,12 +370,15 @@ __global__ __launch_bounds__(Shape<D>::kThreads) __attribute__((amdgpu_waves_per
                 const f32x16 dp = rows_times<D>(vbase, off, gop);
                 // Register 4 j + e holds key key0 + 8 j + 4 half + e.  Keys past
                 // N have zero K and V rows: their dS multiplies a zero K row.
-                const bool masked = CAUSAL && key0 + kRows - 1 > qw0;
+                const bool masked = CAUSAL && MASKED && key0 + kRows - 1 > qw0;
+                // Key key0 + 8 (r >> 2) + 4 half + (r & 3) is masked iff
+                // 8 (r >> 2) + (r & 3) > thr.
+                const int thr = masked ? qidx - key0 - 4 * half : kRows;
                 float p[16], ds[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.c_log2, -l2));
-                    p[r] = (masked & (key0 + 8 * (r >> 2) + 4 * half + (r & 3) > qidx)) ? 0.f : p[r];
+                    p[r] = (8 * (r >> 2) + (r & 3) > thr) ? 0.f : p[r];
                 }
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
@@ -399,10 +404,18 @@ __global__ __launch_bounds__(Shape<D>::kThreads) __attribute__((amdgpu_waves_per
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         };
-        for (int t = 0; t < t_end; t += 2) {
-            tile(t, std::integral_constant<int, 0>{});
+        // Causal: key tiles before q0 are visible to every query of the
+        // workgroup (q0 is a multiple of two tiles, so they come in pairs).
+        const int t_free = CAUSAL ? q0 / kTile : 0;
+        int t = 0;
+        for (; t < t_free; t += 2) {
+            tile(t, std::integral_constant<int, 0>{}, std::false_type{});
+            tile(t + 1, std::integral_constant<int, 1>{}, std::false_type{});
+        }
+        for (; t < t_end; t += 2) {
+            tile(t, std::integral_constant<int, 0>{}, std::true_type{});
             if (t + 1 < t_end)
-                tile(t + 1, std::integral_constant<int, 1>{});
+                tile(t + 1, std::integral_constant<int, 1>{}, std::true_type{});
         }
         if (q_ok)
             store_rows<D>(a.dQ + head + (size_t)qidx * D, dq, a.scale, half);
@@ -509,6 +522,8 @@ __global__ __launch_bounds__(Shape<D>::kThreads) __attribute__((amdgpu_waves_per
                 // past N have zero Q and dO rows and L2 = D = 0: p = 1 there,
                 // but both products it feeds multiply a zero row.
                 const bool masked = CAUSAL && qs0 < kw0 + kRows - 1;
+                // Query qs0 + 8 j + 4 half + e is masked iff 8 j + e < thr.
+                const int thr = masked ? kidx - qs0 - 4 * half : 0;
                 float p[16], ds[16];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -519,7 +534,7 @@ __global__ __launch_bounds__(Shape<D>::kThreads) __attribute__((amdgpu_waves_per
                     for (int e = 0; e < 4; ++e) {
                         const int r = 4 * j + e;
                         float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.c_log2, -l4[e]));
-                        pr = (masked & (qs0 + 8 * j + 4 * half + e < kidx)) ? 0.f : pr;
+                        pr = (8 * j + e < thr) ? 0.f : pr;
                         p[r] = pr;
                         ds[r] = pr * (dp[r] - d4[e]);
                     }
