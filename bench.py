@@ -392,7 +392,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="long_causal",
                     help="name of a workload in exact_io_aware_27_amd.inputs.WORKLOADS")
-    ap.add_argument("--cpu-rows", type=int, default=1024,
+    ap.add_argument("--cpu-rows", type=int, default=5120,
                     help="query rows per head in the oracle's CPU-baseline sample (0: skip)")
     ap.add_argument("--splitkv", default=None,
                     help="measure attn_fwd_splitkv on a workload of exact_io_aware_27_amd.inputs.SPLITKV_WORKLOADS")
