@@ -554,6 +554,46 @@ __global__ __launch_bounds__(Tile<D>::kThreads) __attribute__((amdgpu_waves_per_
         using Unmasked = std::false_type;
         using Masked = std::true_type;
 
+        // In the tiles that need the mask for some query of the workgroup, each
+        // step picks its code for this wave alone: a 32-key block whose every
+        // key is visible to all 32 queries of the wave (below the wave's own
+        // diagonal and inside the key range) needs neither the masked exps nor
+        // the masked row max (which also asks for a positive scale), so only
+        // the blocks that cross the wave's diagonal or the range end pay for
+        // the mask.  The choice is wave-uniform.
+        const int vis_lim = c_log2 > 0.f ? min(CAUSAL ? qw0 + delta : 0x7fffffff, kv_hi - 1) : -1;
+        auto full = [&](int kb) __attribute__((always_inline)) { return 32 * kb + 31 <= vis_lim; };
+        auto mstep = [&](int k, const char *kbuf, int kq, const char *vbuf, int vp, auto loads_tag, int load_t,
+                         char *kdst, char *vdst) __attribute__((always_inline)) {
+            if (full(k + 1))
+                step(k, kbuf, kq, vbuf, vp, Unmasked{}, Unmasked{}, loads_tag, load_t, kdst, vdst);
+            else if (full(k))
+                step(k, kbuf, kq, vbuf, vp, Unmasked{}, Masked{}, loads_tag, load_t, kdst, vdst);
+            else
+                step(k, kbuf, kq, vbuf, vp, Masked{}, Masked{}, loads_tag, load_t, kdst, vdst);
+        };
+        // A masked tile.  Under the causal mask its odd step is dead for this
+        // wave when block 2t, the one whose P V that step takes, is already past
+        // the wave's last visible key: block 2t then has p = 0 everywhere, the
+        // step would add nothing to O, l or lb, and no row can move its
+        // reference on the invisible block 2t+1.  The wave then only makes the
+        // step's copies, and every later tile is dead for it as well.
+        auto tile_m = [&](int t, auto parity_tag) __attribute__((always_inline)) {
+            constexpr int P = decltype(parity_tag)::value;
+            constexpr int kHalf = 32 * T::kRowBytes;
+            char *kp = P ? sk1 : sk0, *kq = P ? sk0 : sk1;
+            char *vp = P ? sv1 : sv0, *vq = P ? sv0 : sv1;
+            mstep(2 * t, kp, kHalf, vq, kHalf, std::false_type{}, 0, kp, vq);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (CAUSAL && 2 * t > last_live) {
+                load_tile(Kh, (t + 2) * kBc, kp, kdma);
+                load_tile(Vh, (t + 1) * kBc, vq, vdma);
+            } else {
+                mstep(2 * t + 1, kq, 0, vp, 0, std::true_type{}, t + 1, kp, vq);
+            }
+        };
+
         // Tiles [t_lo, t_free) need no mask: inside the key range and below the
         // causal diagonal of every query of the workgroup (and a positive scale,
         // which the unmasked row max assumes).  t_free - t_lo is made even so
@@ -586,14 +626,20 @@ __global__ __launch_bounds__(Tile<D>::kThreads) __attribute__((amdgpu_waves_per_
                 tile(t + 1, P1{}, Unmasked{}, Masked{});
                 t += 2;
             }
+            // (Without the causal mask only a ragged end is masked: those tiles
+            // keep the one masked step code.)
             for (; t < t_end; t += 2) {
                 if (dead(t))
                     ghost(t, P0{});
+                else if constexpr (CAUSAL)
+                    tile_m(t, P0{});
                 else
                     tile(t, P0{}, Masked{}, Masked{});
                 if (t + 1 < t_end) {
                     if (dead(t + 1))
                         ghost(t + 1, P1{});
+                    else if constexpr (CAUSAL)
+                        tile_m(t + 1, P1{});
                     else
                         tile(t + 1, P1{}, Masked{}, Masked{});
                 }
