@@ -184,7 +184,7 @@ def bench_splitkv(args):
     out = {"metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-           "config": {"workload": w.describe(), "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+           "config": {"workload": w.describe(splits), "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
                       "causal": w.causal, "splits": splits, "seed": w.seed},
            "roofline": roof, "one_range": {"value": round(one_range, 2), "unit": unit, "ms_per_step": round(ms1, 5)}}
     if args.cpu_rows > 0:

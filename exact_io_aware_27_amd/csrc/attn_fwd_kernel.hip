@@ -85,10 +85,13 @@ constexpr int kBc = 64;      // keys per K/V tile (two 32-key blocks)
 // tile copied into LDS serves twice the queries, which halves the L2->LDS
 // copy traffic per flop (the copies cost shader clock under the chip's power
 // limit).  d = 64: 4 waves (128 queries), two workgroups per CU, so that the
-// smaller d = 64 problems still fill the chip.
-template <int D>
+// smaller d = 64 problems still fill the chip.  Split-key decoding at
+// d = 128 (few query rows, so most waves of a workgroup only copy) takes
+// 4 waves as well: two workgroups per CU then put two computing waves on
+// every CU instead of one.
+template <int D, int W = (D == 128 ? 8 : 4)>
 struct Tile {
-    static constexpr int kWaves = D == 128 ? 8 : 4;
+    static constexpr int kWaves = W;
     static constexpr int kThreads = kWave * kWaves;
     static constexpr int kBr = kRowsPerWave * kWaves;  // query rows per workgroup
     static constexpr int kRowBytes = D * 2;
@@ -162,14 +165,14 @@ struct KArgs {
 // exactly that: without it the scheduler keeps a step in source order
 // whenever the interleaved MFMA/softmax order would cross the three-wave
 // register threshold (168 VGPRs), which costs up to 8%.
-template <int D, bool CAUSAL, bool SPLIT>
-__global__ __launch_bounds__(Tile<D>::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(
+template <int D, bool CAUSAL, bool SPLIT, int W>
+__global__ __launch_bounds__((Tile<D, W>::kThreads)) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(
     const KArgs a)
 {
     // The body is device code only (gfx950 buffer resources and LDS builtins);
     // the host pass needs just the declaration to emit the launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
-    using T = Tile<D>;
+    using T = Tile<D, W>;
     // LDS: K buffers 0, 1 and V buffers 0, 1, each one 64-key tile, as four
     // separate arrays (see the header comment).
     __shared__ __attribute__((aligned(1024))) char sk0[T::kBytes];
@@ -627,18 +630,22 @@ __global__ __launch_bounds__(Tile<D>::kThreads) __attribute__((amdgpu_waves_per_
                 t += 2;
             }
             // (Without the causal mask only a ragged end is masked: those tiles
-            // keep the one masked step code.)
+            // keep the one masked step code.  So does the 4-wave d = 128 decoding
+            // instance, whose masked tiles are at most the last one or two of a
+            // key range: with the per-wave choice the compiler kept its masked
+            // step in source order.)
+            constexpr bool kPerWaveMask = CAUSAL && !(D == 128 && W == 4);
             for (; t < t_end; t += 2) {
                 if (dead(t))
                     ghost(t, P0{});
-                else if constexpr (CAUSAL)
+                else if constexpr (kPerWaveMask)
                     tile_m(t, P0{});
                 else
                     tile(t, P0{}, Masked{}, Masked{});
                 if (t + 1 < t_end) {
                     if (dead(t + 1))
                         ghost(t + 1, P1{});
-                    else if constexpr (CAUSAL)
+                    else if constexpr (kPerWaveMask)
                         tile_m(t + 1, P1{});
                     else
                         tile(t + 1, P1{}, Masked{}, Masked{});
@@ -736,10 +743,10 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float *__restrict
         LSE[row] = wsum > 0.f ? m + __builtin_logf(wsum) : kNegInf;
 }
 
-template <int D, bool CAUSAL, bool SPLIT>
+template <int D, bool CAUSAL, bool SPLIT, int W = Tile<D>::kWaves>
 static hipError_t launch(const AttnLaunch &a, int splits, int split_keys)
 {
-    using T = Tile<D>;
+    using T = Tile<D, W>;
     KArgs k;
     k.Q = (const __bf16 *)a.q;
     k.K = (const __bf16 *)a.k;
@@ -756,7 +763,7 @@ static hipError_t launch(const AttnLaunch &a, int splits, int split_keys)
     k.split_keys = split_keys;
     k.n_wg = (int)(a.BH * (CAUSAL ? (k.nqt + 1) / 2 : k.nqt) * splits);
     k.c_log2 = a.scale * kLog2e;
-    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, SPLIT>), dim3(k.n_wg), dim3(T::kThreads), 0, a.stream, k);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, SPLIT, W>), dim3(k.n_wg), dim3(T::kThreads), 0, a.stream, k);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || !SPLIT)
         return err;
@@ -773,6 +780,10 @@ static hipError_t launch_mode(const AttnLaunch &a)
     const int64_t splits = attn_splits_used(a.Nk, a.num_splits);
     if (splits <= 1)
         return launch<D, CAUSAL, false>(a, 1, (int)attn_split_keys(a.Nk, 1));
+    if constexpr (D == 128) {
+        if (a.Nq <= 128)  // decoding: one 4-wave query tile per head and range
+            return launch<D, CAUSAL, true, 4>(a, (int)splits, (int)attn_split_keys(a.Nk, a.num_splits));
+    }
     return launch<D, CAUSAL, true>(a, (int)splits, (int)attn_split_keys(a.Nk, a.num_splits));
 }
 

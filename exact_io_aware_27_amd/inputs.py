@@ -91,10 +91,10 @@ class SplitWorkload:
         """K and V read once (bf16)."""
         return 2 * 2 * self.B * self.H * self.Nk * self.d
 
-    def describe(self):
+    def describe(self, splits=None):
         return "%s B=%d H=%d Nq=%d Nk=%d d=%d %s splits=%d" % (
             self.name, self.B, self.H, self.Nq, self.Nk, self.d,
-            "causal" if self.causal else "non-causal", self.splits)
+            "causal" if self.causal else "non-causal", self.splits if splits is None else splits)
 
 
 # Split-KV workloads: decoding (one new query per head against 64K cached

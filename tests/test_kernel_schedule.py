@@ -22,8 +22,9 @@ from exact_io_aware_27_amd import build
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL = os.path.join(ROOT, "exact_io_aware_27_amd", "csrc", "attn_fwd_kernel.hip")
-INSTANCES = ["_ZN11attn_gfx95015attn_fwd_kernelILi%dELb%dELb%dEEEvNS_5KArgsE" % (d, c, s)
-             for d in (128, 64) for c in (1, 0) for s in (0, 1)]
+INSTANCES = ["_ZN11attn_gfx95015attn_fwd_kernelILi%dELb%dELb%dELi%dEEEvNS_5KArgsE" % (d, c, s, w)
+             for d in (128, 64) for c in (1, 0) for s in (0, 1) for w in ((8, 4) if d == 128 and s else
+                                                                            (8,) if d == 128 else (4,))]
 SKIP = re.compile(r"^\s*(;|$)")
 
 
