@@ -79,6 +79,9 @@ constexpr int kBc = 64;      // keys per K/V tile (two 32-key blocks)
 // the true running max by up to kRefSlack (log2 units): p <= 2^16.  A row
 // whose next block would exceed that moves the reference to its exact max.
 [[maybe_unused]] constexpr float kRefSlack = 16.f;
+// d = 64 checks each block's own sums instead: a lane's 16 probabilities
+// may add up to at most 2^16 against the reference.
+[[maybe_unused]] constexpr float kSumLimit = 65536.f;
 
 // Workgroup shape per head dim.  d = 128: 8 waves (256 queries), one
 // workgroup per CU, two waves per SIMD from the same workgroup: each K/V
@@ -173,6 +176,10 @@ __global__ __launch_bounds__((Tile<D, W>::kThreads)) __attribute__((amdgpu_waves
     // the host pass needs just the declaration to emit the launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
     using T = Tile<D, W>;
+    // d = 64 guards the lagging reference with a check of each block's own
+    // sums; d = 128 with the next block's row max (free there: it fills VALU
+    // slots that wait on the matrix cores anyway).
+    constexpr bool kSumCheck = D == 64;
     // LDS: K buffers 0, 1 and V buffers 0, 1, each one 64-key tile, as four
     // separate arrays (see the header comment).
     __shared__ __attribute__((aligned(1024))) char sk0[T::kBytes];
@@ -380,6 +387,47 @@ __global__ __launch_bounds__((Tile<D, W>::kThreads)) __attribute__((amdgpu_waves
             }
         };
 
+        // The probabilities of block k (scores s, reference m_sub): P as bf16 in
+        // the B-operand order of the P V MFMA, the sum rs of the fp32 p and the
+        // sum rb of the bf16-rounded p over this lane's 16 keys.
+        // Register 4j+e holds key 32 k + 8 j + 4 half + e.
+        auto block_softmax = [&](const f32x16 &s, float msub, int k, auto masked_tag, bf16x8 *pbo, float &rs,
+                                 float &rb) __attribute__((always_inline)) {
+            constexpr bool MASKED = decltype(masked_tag)::value;
+            float p[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -msub));
+                if constexpr (MASKED)
+                    p[r] = visible(k, r) ? p[r] : 0.f;
+            }
+            float rs0 = p[0], rs1 = p[1];
+#pragma unroll
+            for (int r = 2; r < 16; r += 2) {
+                rs0 += p[r];
+                rs1 += p[r + 1];
+            }
+            // The bf16 pairs are summed from the scalar words: summing from the
+            // elements of the packed vector (w[e] in a loop) gets all four dot
+            // products fed the first element by the compiler.
+            float rb0 = 0.f, rb1 = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const uint32_t w0 = pack_bf16x2(p[8 * ks + 0], p[8 * ks + 1]);
+                const uint32_t w1 = pack_bf16x2(p[8 * ks + 2], p[8 * ks + 3]);
+                const uint32_t w2 = pack_bf16x2(p[8 * ks + 4], p[8 * ks + 5]);
+                const uint32_t w3 = pack_bf16x2(p[8 * ks + 6], p[8 * ks + 7]);
+                rb0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), kOnes, rb0, false);
+                rb1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), kOnes, rb1, false);
+                rb0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), kOnes, rb0, false);
+                rb1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), kOnes, rb1, false);
+                const u32x4 w = {w0, w1, w2, w3};
+                pbo[ks] = __builtin_bit_cast(bf16x8, w);
+            }
+            rs = rs0 + rs1;
+            rb = rb0 + rb1;
+        };
+
         // One 32-key pipeline step (block k): the softmax of block k on the VALU
         // interleaves with the matrix-core work of the scores of block k+1 (K rows
         // from byte kq of buffer kbuf) and P V of block k-1 (V rows from byte vp of
@@ -408,45 +456,20 @@ __global__ __launch_bounds__((Tile<D, W>::kThreads)) __attribute__((amdgpu_waves
             // from the MFMAs it is meant to overlap.
             asm volatile("" : "+v"(sc));
 
-            // Register 4j+e holds key 32 k + 8 j + 4 half + e.  This block's P
-            // is taken against m_sub (the reference max, log2 units), fixed
-            // before the step, so the exps need nothing from this block's max:
-            // the previous step checked that every visible p stays <= 2^kRefSlack.
+            // This block's P is taken against m_sub (the reference max, log2
+            // units), fixed before the step, so the exps need nothing from this
+            // block's max.  d = 128: the previous step checked that every
+            // visible p stays <= 2^kRefSlack.  d = 64: this step checks its own
+            // sums after the exps and, in the rare case, takes the block again.
             // l sums the fp32 p (for the LSE), lb the bf16-rounded p that P V
             // actually multiplies (for O).
-            float p[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], c_log2, -m_sub));
-                if constexpr (MASKED)
-                    p[r] = visible(k, r) ? p[r] : 0.f;
-            }
-            float rs0 = p[0], rs1 = p[1];
-#pragma unroll
-            for (int r = 2; r < 16; r += 2) {
-                rs0 += p[r];
-                rs1 += p[r + 1];
-            }
-            // The bf16 pairs are summed from the scalar words: summing from the
-            // elements of the packed vector (w[e] in a loop) gets all four dot
-            // products fed the first element by the compiler.
             bf16x8 pb[2];
-            float rb0 = 0.f, rb1 = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const uint32_t w0 = pack_bf16x2(p[8 * ks + 0], p[8 * ks + 1]);
-                const uint32_t w1 = pack_bf16x2(p[8 * ks + 2], p[8 * ks + 3]);
-                const uint32_t w2 = pack_bf16x2(p[8 * ks + 4], p[8 * ks + 5]);
-                const uint32_t w3 = pack_bf16x2(p[8 * ks + 6], p[8 * ks + 7]);
-                rb0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), kOnes, rb0, false);
-                rb1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), kOnes, rb1, false);
-                rb0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), kOnes, rb0, false);
-                rb1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), kOnes, rb1, false);
-                const u32x4 w = {w0, w1, w2, w3};
-                pb[ks] = __builtin_bit_cast(bf16x8, w);
+            float rs, rb;
+            block_softmax(sc, m_sub, k, masked_tag, pb, rs, rb);
+            if constexpr (!kSumCheck) {
+                l_run += rs;
+                lb_run += rb;
             }
-            l_run += rs0 + rs1;
-            lb_run += rb0 + rb1;
 
             if constexpr (LOADS) {
                 load_tile(Kh, (load_t + 1) * kBc, kdst, kdma);
@@ -459,22 +482,28 @@ __global__ __launch_bounds__((Tile<D, W>::kThreads)) __attribute__((amdgpu_waves
                                                              sn, 0, 0, 0);
             pv(vbuf, vp, pb_prev);
 
-            // Row max of the next block (this lane's half of its keys, log2
-            // units), for the next step's reference.
-            float mx;
-            if constexpr (NEXT_MASKED) {
-                mx = kNegInf;
+            // d = 128: row max of the next block (this lane's half of its keys,
+            // log2 units), for the next step's reference.  d = 64: whether some
+            // lane's sum of this block passed kSumLimit (inf included).
+            float mx = kNegInf;
+            bool reref = false;
+            if constexpr (kSumCheck) {
+                reref = __builtin_amdgcn_ballot_w64(rs > kSumLimit) != 0;  // wave-uniform
+            } else {
+                if constexpr (NEXT_MASKED) {
+                    mx = kNegInf;
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    mx = fmaxf(mx, visible(k + 1, r) ? sn[r] * c_log2 : kNegInf);
-            } else {  // every key visible and c_log2 > 0
-                float r0 = sn[0];
+                    for (int r = 0; r < 16; ++r)
+                        mx = fmaxf(mx, visible(k + 1, r) ? sn[r] * c_log2 : kNegInf);
+                } else {  // every key visible and c_log2 > 0
+                    float r0 = sn[0];
 #pragma unroll
-                for (int r = 1; r < 16; ++r)
-                    r0 = fmaxf(r0, sn[r]);
-                mx = r0 * c_log2;
+                    for (int r = 1; r < 16; ++r)
+                        r0 = fmaxf(r0, sn[r]);
+                    mx = r0 * c_log2;
+                }
+                reref = __builtin_amdgcn_ballot_w64(mx > m_thr) != 0;  // wave-uniform
             }
-            const bool reref = __builtin_amdgcn_ballot_w64(mx > m_thr) != 0;  // wave-uniform
 
             // Issue order for this step's scheduling region: the 16 MFMAs (8 for
             // the next scores, 8 for P V) each followed by a share of the softmax
@@ -494,26 +523,57 @@ __global__ __launch_bounds__((Tile<D, W>::kThreads)) __attribute__((amdgpu_waves
             // Keep this block's P and row sums inside this step: otherwise the
             // compiler sinks the exps and adds next to their first uses (the next
             // step's P V and the loop latch), where no MFMA is left to hide them.
-            asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(l_run), "+v"(lb_run));
+            if constexpr (kSumCheck)
+                asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(rs), "+v"(rb));
+            else
+                asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(l_run), "+v"(lb_run));
 
-            // The reference moved at the previous step: O now holds P V of block
-            // k-1 as well, taken against the old reference, so rescale it here.
-            if (pending) {
+            if constexpr (kSumCheck) {
+                // Some lane's probabilities of this block passed kSumLimit against
+                // the reference: move the reference to the row's exact running max
+                // (this block's scores are still in registers), rescale l, lb and
+                // O (which now holds P V up to block k-1, all against the old
+                // reference), and take this block's probabilities again.
+                if (reref) {
+                    float mb = kNegInf;
 #pragma unroll
-                for (int b = 0; b < T::kOBlocks; ++b)
-                    oacc[b] *= alpha_pend;
-            }
-            // Some row of the next block has a p above 2^kRefSlack against the
-            // current reference: move the reference to the row's exact running
-            // max (both halves of the row) and rescale the sums now, O after the
-            // next P V.
-            pending = reref;
-            if (reref) {
-                const float m_new = fmaxf(m_ref, wave_half_max(mx));
-                alpha_pend = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-                l_run *= alpha_pend;
-                lb_run *= alpha_pend;
-                set_ref(m_new);
+                    for (int r = 0; r < 16; ++r) {
+                        const float t = sc[r] * c_log2;
+                        mb = fmaxf(mb, (!MASKED || visible(k, r)) ? t : kNegInf);
+                    }
+                    const float m_new = fmaxf(m_ref, wave_half_max(mb));
+                    const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+                    l_run *= alpha;
+                    lb_run *= alpha;
+#pragma unroll
+                    for (int b = 0; b < T::kOBlocks; ++b)
+                        oacc[b] *= alpha;
+                    set_ref(m_new);
+                    block_softmax(sc, m_sub, k, masked_tag, pb, rs, rb);
+                }
+                l_run += rs;
+                lb_run += rb;
+            } else {
+                // The reference moved at the previous step: O now holds P V of
+                // block k-1 as well, taken against the old reference, so rescale
+                // it here.
+                if (pending) {
+#pragma unroll
+                    for (int b = 0; b < T::kOBlocks; ++b)
+                        oacc[b] *= alpha_pend;
+                }
+                // Some row of the next block has a p above 2^kRefSlack against the
+                // current reference: move the reference to the row's exact running
+                // max (both halves of the row) and rescale the sums now, O after
+                // the next P V.
+                pending = reref;
+                if (reref) {
+                    const float m_new = fmaxf(m_ref, wave_half_max(mx));
+                    alpha_pend = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+                    l_run *= alpha_pend;
+                    lb_run *= alpha_pend;
+                    set_ref(m_new);
+                }
             }
             sc = sn;
             pb_prev[0] = pb[0];

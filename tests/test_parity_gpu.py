@@ -106,6 +106,21 @@ def test_ragged_lengths(N, d, causal):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
+def test_growing_scores_move_the_reference(d, causal):
+    """Large logits (Q, K ~ N(0, 4^2)) on keys whose norm grows along the
+    sequence: each row's running max rises many times by more than the
+    kernel's slack, so the reference moves again and again (d = 128 decides
+    it from the next block's row max, d = 64 from each block's own sums and
+    takes the block's probabilities again)."""
+    N = 1000
+    q, k, v = inputs.make_qkv(1, 2, N, d, seed=3000 + d + causal, sigma_qk=4.0)
+    ramp = torch.linspace(0.25, 2.0, N, dtype=torch.float32)[None, None, :, None]
+    k = (k.float() * ramp).to(torch.bfloat16)
+    check_full(q, k, v, causal, 1.0 / math.sqrt(d), "growing scores d=%d" % d)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 33, 100, 1000])
 def test_memory_past_the_sequence_is_never_read(N, d, causal):
     """K and V sit at the start of a NaN-filled allocation, so every row past
