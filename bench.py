@@ -471,7 +471,9 @@ def main():
     traffic = measured_traffic()
     props = torch.cuda.get_device_properties(dev)
     out = {
-        "metric": METRIC,
+        # the headline metric on its own workload; another workload names itself
+        "metric": METRIC if w.name == "long_causal" else
+        "attn fwd TFLOP/s + %% of bf16 MFMA peak, 1 GPU, %s" % w.describe(),
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
