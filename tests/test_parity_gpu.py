@@ -154,10 +154,15 @@ def test_many_heads_and_batches(d):
     check_full(q, k, v, True, 1.0 / math.sqrt(d), "B=3 H=5 N=300")
 
 
-def test_scale_argument_is_used():
-    q, k, v = inputs.make_qkv(1, 2, 257, 128, seed=78)
-    check_full(q, k, v, False, 0.37, "scale 0.37")
-    check_full(q, k, v, True, 0.01, "scale 0.01")
+@pytest.mark.parametrize("d", [64, 128])
+def test_scale_argument_is_used(d):
+    """Positive scales, and non-positive ones, which send every tile through
+    the masked code (the unmasked row max assumes a positive scale)."""
+    q, k, v = inputs.make_qkv(1, 2, 257, d, seed=78 + d)
+    check_full(q, k, v, False, 0.37, "scale 0.37 d=%d" % d)
+    check_full(q, k, v, True, 0.01, "scale 0.01 d=%d" % d)
+    check_full(q, k, v, True, -0.25, "scale -0.25 d=%d" % d)
+    check_full(q, k, v, False, 0.0, "scale 0 d=%d" % d)
 
 
 @pytest.mark.parametrize("d", [64, 128])
