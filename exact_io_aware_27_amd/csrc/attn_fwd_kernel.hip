@@ -13,8 +13,9 @@
 //
 // gfx950 mapping
 //   * 32 query rows per 64-lane wave.  d = 128: 8 waves (256 queries) per
-//     workgroup, one workgroup per CU; d = 64: 4 waves (128 queries), two
-//     workgroups per CU.  Either way two waves share each SIMD.
+//     workgroup, one workgroup per CU; d = 64, and key ranges of a few query
+//     rows (decoding) at d = 128: 4 waves (128 queries), two workgroups per
+//     CU.  Either way two waves share each SIMD.
 //   * Each wave computes the TRANSPOSED score tile S^T = K Q^T with
 //     v_mfma_f32_32x32x16_bf16: in the 32x32 accumulator layout a lane holds
 //     one column (one query) and 16 of the 32 rows (keys), so a query's row
@@ -44,11 +45,14 @@
 //     Probabilities are taken against a reference max that may lag the
 //     exact running max by up to 16 (log2 units), the conditional rescaling
 //     of the FlashAttention-4 section of the cheat sheet: the exps of a block
-//     never wait for its own max.  Each step computes the row max of the
-//     NEXT block from its fresh scores (during the P V MFMAs); a row that
-//     would pass the slack moves the reference to its exact max, a rare
+//     never wait for its own max.  d = 128: each step computes the row max
+//     of the NEXT block from its fresh scores (during the P V MFMAs); a row
+//     that would pass the slack moves the reference to its exact max, a rare
 //     wave-uniform branch that rescales the sums at once and O after the
-//     next P V.  With a lagging reference the largest p is not 1 and its
+//     next P V.  d = 64 (VALU-bound: half the MFMAs per step for the same
+//     softmax work): each step checks its own block's sums after the exps
+//     instead, and the rare branch moves the reference, rescales l, lb and
+//     O, and takes the block again from its scores.  With a lagging reference the largest p is not 1 and its
 //     bf16 rounding is not exact, so O is divided by the sum of the
 //     bf16-rounded probabilities that built it (v_dot2c_f32_bf16 against
 //     ones), which keeps a one-hot row exact; the LSE uses the fp32 sum.
