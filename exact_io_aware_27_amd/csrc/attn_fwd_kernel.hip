@@ -164,6 +164,7 @@ struct KArgs {
     float *LSE;
     float *Opart, *LSEpart;
     int BH, Nq, Nk, n_wg, nqt, n_splits, split_keys;
+    int lpt;  // causal, one key range: single query tiles, longest first
     float c_log2;
 };
 
@@ -207,15 +208,29 @@ __global__ __launch_bounds__((Tile<D, W>::kThreads)) __attribute__((amdgpu_waves
     // middle tile of an odd count is alone); non-causal: one tile per unit.
     // Work items are ordered (head, split, unit), so that all the work on one
     // head's keys stays on one XCD.
-    const int n_units = CAUSAL ? (nqt + 1) / 2 : nqt;
+    //
+    // A causal grid too small to fill the chip twice over with pairs (or a
+    // few query tiles per head) runs single tiles instead, longest first
+    // within each XCD: XCD x owns heads [x B H / 8, (x + 1) B H / 8), and its
+    // workgroups walk them tile by tile from the heaviest (the host chooses
+    // this only when 8 divides B H).  Uneven work then fills the slots the
+    // pairs would have left idle.
+    const bool lpt = CAUSAL && !SPLIT && a.lpt;
+    const int n_units = (CAUSAL && !lpt) ? (nqt + 1) / 2 : nqt;
     int bh, rem;
-    unit_of(blockIdx.x, a.n_wg, n_units * a.n_splits, bh, rem);
+    if (lpt) {
+        const int hpx = a.BH / kXcds, xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+        bh = xcd * hpx + slot % hpx;
+        rem = (nqt - 1) - slot / hpx;
+    } else {
+        unit_of(blockIdx.x, a.n_wg, n_units * a.n_splits, bh, rem);
+    }
     const int split = rem / n_units, unit = rem % n_units;
     const int kv_lo = split * a.split_keys;
     const int kv_hi = min(Nk, kv_lo + a.split_keys);
-    const int npass = (CAUSAL && nqt - 1 - unit != unit) ? 2 : 1;
+    const int npass = (CAUSAL && !lpt && nqt - 1 - unit != unit) ? 2 : 1;
     for (int pass = 0; pass < npass; ++pass) {
-        const int qt = CAUSAL ? (pass == 0 ? nqt - 1 - unit : unit) : unit;
+        const int qt = (CAUSAL && !lpt) ? (pass == 0 ? nqt - 1 - unit : unit) : unit;
         if (pass > 0)
             __syncthreads();  // every wave is done with the previous tile's LDS
         const int q0 = qt * T::kBr;
@@ -825,7 +840,13 @@ static hipError_t launch(const AttnLaunch &a, int splits, int split_keys)
     k.nqt = (int)((a.Nq + T::kBr - 1) / T::kBr);
     k.n_splits = splits;
     k.split_keys = split_keys;
-    k.n_wg = (int)(a.BH * (CAUSAL ? (k.nqt + 1) / 2 : k.nqt) * splits);
+    // Causal, one key range: pairs of query tiles, or single tiles longest
+    // first when the pairs would not fill the chip's workgroup slots twice
+    // (256 CUs, 8 / W workgroups each) and the heads split evenly over the
+    // XCDs.
+    const int64_t pairs = a.BH * ((k.nqt + 1) / 2);
+    k.lpt = CAUSAL && !SPLIT && a.BH % kXcds == 0 && pairs < 2 * 256 * (8 / W);
+    k.n_wg = (int)(a.BH * ((CAUSAL && !k.lpt) ? (k.nqt + 1) / 2 : k.nqt) * splits);
     k.c_log2 = a.scale * kLog2e;
     hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, SPLIT, W>), dim3(k.n_wg), dim3(T::kThreads), 0, a.stream, k);
     hipError_t err = hipGetLastError();

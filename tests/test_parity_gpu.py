@@ -155,6 +155,16 @@ def test_many_heads_and_batches(d):
 
 
 @pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [777, 1024])
+def test_small_causal_grid_single_tiles_longest_first(d, N):
+    """8 | B H and too few heavy+light pairs to fill the chip twice: the
+    launch runs single query tiles, longest first within each XCD (odd and
+    even tile counts, a ragged last tile)."""
+    q, k, v = inputs.make_qkv(2, 4, N, d, seed=6000 + N + d)
+    check_full(q, k, v, True, 1.0 / math.sqrt(d), "B=2 H=4 N=%d d=%d causal" % (N, d))
+
+
+@pytest.mark.parametrize("d", [64, 128])
 def test_scale_argument_is_used(d):
     """Positive scales, and non-positive ones, which send every tile through
     the masked code (the unmasked row max assumes a positive scale)."""
