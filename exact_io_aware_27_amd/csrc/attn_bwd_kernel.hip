@@ -111,6 +111,7 @@ struct BArgs {
     float *L2, *Dsum;
     __bf16 *dQ, *dK, *dV;
     int BH, N, n_wg, ntiles;
+    int lpt;  // causal: single blocks, longest first (see block_of)
     float c_log2, scale;
 };
 
@@ -270,6 +271,26 @@ __device__ __forceinline__ int pair_block(bool causal, int nblk, int unit, int p
     return causal ? (pass == 0 ? nblk - 1 - unit : unit) : unit;
 }
 
+// Workgroup -> (head, unit, passes).  A causal grid too small to fill the
+// chip twice over with pairs runs single blocks instead, longest first within
+// each XCD: XCD x owns heads [x B H / 8, (x + 1) B H / 8) (the host chooses
+// this only when 8 divides B H), and its workgroups walk them block by block
+// from the heaviest; unit r is then the r-th heaviest block, which
+// heavy_block turns into a block index.
+__device__ __forceinline__ void block_of(const BArgs &a, int nblk, bool causal, int &bh, int &unit, int &npass)
+{
+    if (causal && a.lpt) {
+        const int hpx = a.BH / kXcds, xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+        bh = xcd * hpx + slot % hpx;
+        unit = slot / hpx;
+        npass = 1;
+        return;
+    }
+    const int n_units = causal ? (nblk + 1) / 2 : nblk;
+    unit_of(blockIdx.x, a.n_wg, n_units, bh, unit);
+    npass = (causal && nblk - 1 - unit != unit) ? 2 : 1;
+}
+
 // ---------------------------------------------------------------------------
 // dQ (and D, L2): one workgroup per query block of one head.  Per 32-key
 // block: S^T = K Q^T and dP^T = V dO^T (keys x queries), P^T = exp2(S^T
@@ -290,10 +311,8 @@ __global__ __launch_bounds__(Shape<D>::kThreads) __attribute__((amdgpu_waves_per
     const int n = lane & 31, half = lane >> 5;
     const int N = a.N, nblk = a.ntiles;
 
-    const int n_units = CAUSAL ? (nblk + 1) / 2 : nblk;
-    int bh, unit;
-    unit_of(blockIdx.x, a.n_wg, n_units, bh, unit);
-    const int npass = (CAUSAL && nblk - 1 - unit != unit) ? 2 : 1;
+    int bh, unit, npass;
+    block_of(a, nblk, CAUSAL, bh, unit, npass);
     const size_t head = (size_t)bh * (size_t)N * D;
     const __bf16 *Kh = a.K + head, *Vh = a.V + head;
 
@@ -305,7 +324,8 @@ __global__ __launch_bounds__(Shape<D>::kThreads) __attribute__((amdgpu_waves_per
         Offsets<D> off(wave_u, lane_p);
         if (pass > 0)
             __syncthreads();  // every wave is done with the previous block's LDS
-        const int q0 = pair_block(CAUSAL, nblk, unit, pass) * S::kBlock;
+        // (longest first: the heaviest query block is the last)
+        const int q0 = (CAUSAL && a.lpt ? nblk - 1 - unit : pair_block(CAUSAL, nblk, unit, pass)) * S::kBlock;
         const int qw0 = q0 + wave_u * kRows;
         const int qidx = qw0 + n;
         const bool q_ok = qidx < N;
@@ -444,10 +464,8 @@ __global__ __launch_bounds__(Shape<D>::kThreads) __attribute__((amdgpu_waves_per
     const int n = lane & 31, half = lane >> 5;
     const int N = a.N, nblk = a.ntiles;
 
-    const int n_units = CAUSAL ? (nblk + 1) / 2 : nblk;
-    int bh, unit;
-    unit_of(blockIdx.x, a.n_wg, n_units, bh, unit);
-    const int npass = (CAUSAL && nblk - 1 - unit != unit) ? 2 : 1;
+    int bh, unit, npass;
+    block_of(a, nblk, CAUSAL, bh, unit, npass);
     const size_t head = (size_t)bh * (size_t)N * D;
     const __bf16 *Qh = a.Q + head, *Gh = a.dO + head;
     const float *L2h = a.L2 + (size_t)bh * N, *Dh = a.Dsum + (size_t)bh * N;
@@ -469,7 +487,9 @@ __global__ __launch_bounds__(Shape<D>::kThreads) __attribute__((amdgpu_waves_per
         };
         if (pass > 0)
             __syncthreads();
-        const int k0 = pair_block(CAUSAL, nblk, unit, pass) * S::kBlock;
+        // (longest first: the heaviest key block is the first, which every
+        // query sees)
+        const int k0 = (CAUSAL && a.lpt ? unit : pair_block(CAUSAL, nblk, unit, pass)) * S::kBlock;
         const int kw0 = k0 + wave_u * kRows;
         const int kidx = kw0 + n;
         const bool k_ok = kidx < N;
@@ -580,7 +600,12 @@ static hipError_t launch(const AttnBwdLaunch &l)
     a.N = (int)l.N;
     using S = Shape<D>;
     a.ntiles = (int)((l.N + S::kBlock - 1) / S::kBlock);
-    a.n_wg = (int)(l.BH * (CAUSAL ? (a.ntiles + 1) / 2 : a.ntiles));
+    // Causal: pairs of blocks, or single blocks longest first when the pairs
+    // would not fill the chip's workgroup slots twice (256 CUs, 8 / kWaves
+    // workgroups each) and the heads split evenly over the XCDs.
+    const int64_t pairs = l.BH * ((a.ntiles + 1) / 2);
+    a.lpt = CAUSAL && l.BH % kXcds == 0 && pairs < 2 * 256 * (8 / S::kWaves);
+    a.n_wg = (int)(l.BH * ((CAUSAL && !a.lpt) ? (a.ntiles + 1) / 2 : a.ntiles));
     a.c_log2 = l.scale * kLog2e;
     a.scale = l.scale;
     hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL>), dim3(a.n_wg), dim3(S::kThreads), 0, l.stream, a);

@@ -62,6 +62,15 @@ def test_matches_oracle(B, H, N, d, causal):
     check(q, k, v, g, causal, 1.0 / math.sqrt(d), "B=%d H=%d N=%d d=%d" % (B, H, N, d))
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_small_causal_grid_single_blocks_longest_first(d):
+    """8 | B H and too few heavy+light pairs to fill the chip twice: both
+    kernels run single blocks, longest first within each XCD (the dQ kernel
+    from the last query block, the dK/dV kernel from the first key block)."""
+    q, k, v, g = case(2, 4, 777, d, seed=7000 + d)
+    check(q, k, v, g, True, 1.0 / math.sqrt(d), "B=2 H=4 N=777 d=%d causal" % d)
+
+
 def test_gpt2_small_shape_every_head():
     # 8 x 12 heads of 1024 queries, d = 64, causal: the GPT-2 (seq 1K) shape
     w = [x for x in inputs.WORKLOADS if x.name == "gpt2_small"][0]
