@@ -32,11 +32,21 @@ KERNEL_SOURCES = [os.path.join(ROOT, "exact_io_aware_27_amd", "csrc", f)
                   for f in ("attn_fwd_kernel.hip", "attn_common.h")]  # the forward kernel's own code
 
 
+def code_only(text):
+    """C++ source without its comments and blank lines, so that an edit to a
+    comment does not count as a change of the kernel."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_hash():
+    """Hash of the forward kernel's code (comments excluded)."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p) as f:
+            h.update(code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -52,10 +52,11 @@
 //     next P V.  d = 64 (VALU-bound: half the MFMAs per step for the same
 //     softmax work): each step checks its own block's sums after the exps
 //     instead, and the rare branch moves the reference, rescales l, lb and
-//     O, and takes the block again from its scores.  With a lagging reference the largest p is not 1 and its
-//     bf16 rounding is not exact, so O is divided by the sum of the
-//     bf16-rounded probabilities that built it (v_dot2c_f32_bf16 against
-//     ones), which keeps a one-hot row exact; the LSE uses the fp32 sum.
+//     O, and takes the block again from its scores.  With a lagging
+//     reference the largest p is not 1 and its bf16 rounding is not exact,
+//     so O is divided by the sum of the bf16-rounded probabilities that
+//     built it (v_dot2c_f32_bf16 against ones), which keeps a one-hot row
+//     exact; the LSE uses the fp32 sum.
 //   * Causal: tiles entirely above the diagonal are never loaded; the mask
 //     is applied only in tiles that cross the diagonal or the sequence end.
 //   * Causal load balance: a workgroup runs two query tiles of one head in
