@@ -417,8 +417,8 @@ __global__ __launch_bounds__(Shape<D>::kThreads) __attribute__((amdgpu_waves_per
 #pragma unroll
                 for (int i = 0; i < S::kSteps; ++i) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // dP
-                    __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);
                 }
             }
             __builtin_amdgcn_s_waitcnt(0);

