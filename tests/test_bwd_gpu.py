@@ -63,12 +63,13 @@ def test_matches_oracle(B, H, N, d, causal):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-def test_small_causal_grid_single_blocks_longest_first(d):
+@pytest.mark.parametrize("N", [1, 129, 777])
+def test_small_causal_grid_single_blocks_longest_first(d, N):
     """8 | B H and too few heavy+light pairs to fill the chip twice: both
     kernels run single blocks, longest first within each XCD (the dQ kernel
     from the last query block, the dK/dV kernel from the first key block)."""
-    q, k, v, g = case(2, 4, 777, d, seed=7000 + d)
-    check(q, k, v, g, True, 1.0 / math.sqrt(d), "B=2 H=4 N=777 d=%d causal" % d)
+    q, k, v, g = case(2, 4, N, d, seed=7000 + N + d)
+    check(q, k, v, g, True, 1.0 / math.sqrt(d), "B=2 H=4 N=%d d=%d causal" % (N, d))
 
 
 def test_gpt2_small_shape_every_head():

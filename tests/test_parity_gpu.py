@@ -155,7 +155,7 @@ def test_many_heads_and_batches(d):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("N", [777, 1024])
+@pytest.mark.parametrize("N", [1, 129, 777, 1024, 2049])
 def test_small_causal_grid_single_tiles_longest_first(d, N):
     """8 | B H and too few heavy+light pairs to fill the chip twice: the
     launch runs single query tiles, longest first within each XCD (odd and
