@@ -68,6 +68,22 @@ def test_prefill_splits_match_oracle(N, S, d, causal):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Nq", [1000, 33])
+def test_growing_scores_move_the_reference_in_every_range(Nq, d, causal):
+    """Large logits (Q, K ~ N(0, 4^2)) on keys whose norm grows along the
+    sequence, cut into 3 ranges: the reference moves many times inside each
+    range (d = 128 from the next block's row max, d = 64 from each block's own
+    sums), and the ranges' LSEs then differ by large amounts in the merge."""
+    Nk = 1000
+    q = inputs.make_qkv(1, 2, Nq, d, seed=8000 + Nq + d + causal, sigma_qk=4.0)[0]
+    _, k, v = inputs.make_qkv(1, 2, Nk, d, seed=8100 + Nq + d + causal, sigma_qk=4.0)
+    ramp = torch.linspace(0.25, 2.0, Nk, dtype=torch.float32)[None, None, :, None]
+    k = (k.float() * ramp).to(torch.bfloat16)
+    check(q, k, v, causal, 3, "growing scores Nq=%d d=%d" % (Nq, d))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("Nq,Nk,S", [
     (1, 1, 1), (1, 1, 4), (1, 127, 4), (1, 128, 4), (1, 129, 4), (1, 1000, 1), (1, 1000, 4),
     (1, 4097, 16), (4, 1000, 8), (33, 1000, 3), (33, 4097, 16), (257, 4097, 5)])
