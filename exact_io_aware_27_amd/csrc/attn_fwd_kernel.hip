@@ -45,14 +45,15 @@
 //     Probabilities are taken against a reference max that may lag the
 //     exact running max by up to 16 (log2 units), the conditional rescaling
 //     of the FlashAttention-4 section of the cheat sheet: the exps of a block
-//     never wait for its own max.  d = 128: each step computes the row max
-//     of the NEXT block from its fresh scores (during the P V MFMAs); a row
-//     that would pass the slack moves the reference to its exact max, a rare
-//     wave-uniform branch that rescales the sums at once and O after the
-//     next P V.  d = 64 (VALU-bound: half the MFMAs per step for the same
-//     softmax work): each step checks its own block's sums after the exps
-//     instead, and the rare branch moves the reference, rescales l, lb and
-//     O, and takes the block again from its scores.  With a lagging
+//     never wait for its own max.  Two guards keep p bounded, chosen per
+//     instance by measurement.  The causal instances and d = 64 check each
+//     block's own sums after the exps (3 instructions per step); the rare,
+//     wave-uniform branch moves the reference to the row's exact running
+//     max, rescales l, lb and O, and takes the block again from its scores.
+//     The non-causal d = 128 instances compute the row max of the NEXT
+//     block from its fresh scores (during the P V MFMAs); a row that would
+//     pass the slack moves the reference to its exact max, and the rare
+//     branch rescales the sums at once and O after the next P V.  With a lagging
 //     reference the largest p is not 1 and its bf16 rounding is not exact,
 //     so O is divided by the sum of the bf16-rounded probabilities that
 //     built it (v_dot2c_f32_bf16 against ones), which keeps a one-hot row
@@ -81,11 +82,12 @@ constexpr int kRowsPerWave = 32;
 constexpr int kBrMin = 128;  // fewest query rows per workgroup (d = 64)
 constexpr int kBc = 64;      // keys per K/V tile (two 32-key blocks)
 // A block's probabilities are taken against a reference max that may lag
-// the true running max by up to kRefSlack (log2 units): p <= 2^16.  A row
-// whose next block would exceed that moves the reference to its exact max.
+// the true running max by up to kRefSlack (log2 units): p <= 2^16.  Under the
+// next-block guard a row whose next block would exceed that moves the
+// reference to its exact max.
 [[maybe_unused]] constexpr float kRefSlack = 16.f;
-// d = 64 checks each block's own sums instead: a lane's 16 probabilities
-// may add up to at most 2^16 against the reference.
+// Under the sum check a lane's 16 probabilities of one block may add up to
+// at most 2^16 against the reference.
 [[maybe_unused]] constexpr float kSumLimit = 65536.f;
 
 // Workgroup shape per head dim.  d = 128: 8 waves (256 queries), one
@@ -182,10 +184,18 @@ __global__ __launch_bounds__((Tile<D, W>::kThreads)) __attribute__((amdgpu_waves
     // the host pass needs just the declaration to emit the launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
     using T = Tile<D, W>;
-    // d = 64 guards the lagging reference with a check of each block's own
-    // sums; d = 128 with the next block's row max (free there: it fills VALU
-    // slots that wait on the matrix cores anyway).
-    constexpr bool kSumCheck = D == 64;
+    // The lagging reference's guard.  The check of each block's own sums
+    // costs 3 instructions per step against the next block's row max (about
+    // 11).  Same-box A/B, outputs bitwise equal: the long causal workload ran
+    // 1099 -> 1150 TFLOP/s with the sum check (and 4 VALU per MFMA group,
+    // below); the non-causal large-logit one 1124 -> 1097, as its compiled
+    // step lost the MFMA interleave, so the non-causal d = 128 instances keep
+    // the row max.  d = 64 is VALU-bound and has always used the sum check.
+    constexpr bool kSumCheck = D == 64 || CAUSAL;
+    // VALU instructions placed after each MFMA of a step: 16 x 4 covers the
+    // sum-check step's softmax at d = 128 (about 71 instructions); 5 suits
+    // the longer row-max step and d = 64.
+    constexpr int kValuPerMfma = (D == 128 && kSumCheck) ? 4 : 5;
     // LDS: K buffers 0, 1 and V buffers 0, 1, each one 64-key tile, as four
     // separate arrays (see the header comment).
     __shared__ __attribute__((aligned(1024))) char sk0[T::kBytes];
@@ -537,7 +547,7 @@ __global__ __launch_bounds__((Tile<D, W>::kThreads)) __attribute__((amdgpu_waves
             for (int i = 0; i < 2 * T::kQkSteps; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
-                __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);  // VALU incl. transcendental
+                __builtin_amdgcn_sched_group_barrier(0x402, kValuPerMfma, 0);  // VALU incl. transcendental
                 if (LOADS && i < 2 * T::kLoadsPerWave)
                     __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // tile copy (VMEM)
             }
@@ -649,7 +659,12 @@ __global__ __launch_bounds__((Tile<D, W>::kThreads)) __attribute__((amdgpu_waves
         auto full = [&](int kb) __attribute__((always_inline)) { return 32 * kb + 31 <= vis_lim; };
         auto mstep = [&](int k, const char *kbuf, int kq, const char *vbuf, int vp, auto loads_tag, int load_t,
                          char *kdst, char *vdst) __attribute__((always_inline)) {
-            if (full(k + 1))
+            if constexpr (kSumCheck) {  // the next block's mask matters only to the row-max guard
+                if (full(k))
+                    step(k, kbuf, kq, vbuf, vp, Unmasked{}, Unmasked{}, loads_tag, load_t, kdst, vdst);
+                else
+                    step(k, kbuf, kq, vbuf, vp, Masked{}, Masked{}, loads_tag, load_t, kdst, vdst);
+            } else if (full(k + 1))
                 step(k, kbuf, kq, vbuf, vp, Unmasked{}, Unmasked{}, loads_tag, load_t, kdst, vdst);
             else if (full(k))
                 step(k, kbuf, kq, vbuf, vp, Unmasked{}, Masked{}, loads_tag, load_t, kdst, vdst);
@@ -660,8 +675,8 @@ __global__ __launch_bounds__((Tile<D, W>::kThreads)) __attribute__((amdgpu_waves
         // wave when block 2t, the one whose P V that step takes, is already past
         // the wave's last visible key: block 2t then has p = 0 everywhere, the
         // step would add nothing to O, l or lb, and no row can move its
-        // reference on the invisible block 2t+1.  The wave then only makes the
-        // step's copies, and every later tile is dead for it as well.
+        // reference (its sums are 0).  The wave then only makes the step's
+        // copies, and every later tile is dead for it as well.
         auto tile_m = [&](int t, auto parity_tag) __attribute__((always_inline)) {
             constexpr int P = decltype(parity_tag)::value;
             constexpr int kHalf = 32 * T::kRowBytes;
