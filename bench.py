@@ -395,6 +395,44 @@ def bench_fp8(args):
     return 0
 
 
+def bench_micro(args):
+    """One JSON line of gfx950 issue rates (exact_io_aware_27_amd/micro.py):
+    cycles per VALU instruction by kind and waves per SIMD, dependent-chain
+    latencies, and cycles per 32x32x16 bf16 MFMA when k FMAs and e
+    exponentials follow each one -- the per-unit cycle count the attention
+    kernels are designed against, measured in shader cycles."""
+    import torch
+
+    from exact_io_aware_27_amd import micro
+
+    micro.load()
+    torch.cuda.set_device(0)
+    rates = []
+    for op in ("fma", "mul", "exp", "poly"):
+        for w in (1, 2, 4):
+            r = micro.rate(op, w)
+            print("rate %-4s waves/SIMD %d: %.2f cycles/inst per SIMD  (%.2f GHz)"
+                  % (op, w, r["cycles_per_inst"], r["clock_ghz"]), file=sys.stderr, flush=True)
+            rates.append(r)
+        r = micro.rate(op, 1, dependent=True)
+        print("latency %-4s: %.2f cycles per dependent element" % (op, r["cycles_per_element"]),
+              file=sys.stderr, flush=True)
+        rates.append(r)
+    mixes = []
+    for k, e, poly in micro.MIXES:
+        for w in (1, 2):
+            m = micro.mix(k, e, poly, w)
+            print("mix %d fma + %d %s per MFMA, waves/SIMD %d: %.2f cycles/MFMA, %.0f TFLOP/s (%.2f GHz)"
+                  % (k, e, m["exp"], w, m["cycles_per_mfma"], m["tflops"], m["clock_ghz"]),
+                  file=sys.stderr, flush=True)
+            mixes.append(m)
+    out = {"metric": "gfx950 issue rates (shader cycles), 1 GPU", "unit": "cycles", "rates": rates,
+           "mixes": mixes, "note": "rate: per SIMD over all its waves (independent chains) or per dependent "
+                                  "instruction; mix: per 32x32x16 bf16 MFMA per SIMD (32 = matrix-core rate)"}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -409,6 +447,8 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="key ranges for --splitkv (0: the workload's)")
     ap.add_argument("--bwd", action="store_true", help="measure the backward pass (attn_bwd) on --workload")
     ap.add_argument("--fp8", action="store_true", help="measure the FP8 forward (attn_fwd_fp8) on --workload")
+    ap.add_argument("--micro", action="store_true",
+                    help="gfx950 issue-rate microbenchmarks (VALU, exp, exp2_poly, MFMA mixes) in shader cycles")
     ap.add_argument("--cpu-heads", type=int, default=1,
                     help="--bwd: whole heads in the oracle's CPU-baseline sample (0: skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -434,6 +474,8 @@ def main():
         return bench_bwd(args)
     if args.fp8:
         return bench_fp8(args)
+    if args.micro:
+        return bench_micro(args)
 
     import torch
 

@@ -8,6 +8,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libattn.so")
 SOURCES = ["attn_api.hip", "attn_fwd_kernel.hip", "attn_bwd_kernel.hip", "attn_fp8_kernel.hip"]
+# the issue-rate microbenchmarks (bench.py --micro) and the exp2_poly accuracy
+# kernel: a separate library, not part of the attention ABI
+MICRO_LIB = os.path.join(PKG, "libattn_micro.so")
+MICRO_SOURCES = ["attn_micro.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -19,16 +23,23 @@ FLAGS = [
 ]
 
 
-def build(verbose=False):
-    """Compile every HIP source of the library into exact_io_aware_27_amd/libattn.so."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(lib, sources, verbose):
+    srcs = [os.path.join(CSRC, s) for s in sources]
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC] + FLAGS + ["-o", tmp] + srcs
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose=False):
+    """Compile every HIP source: the attention library
+    (exact_io_aware_27_amd/libattn.so) and the microbenchmark library
+    (exact_io_aware_27_amd/libattn_micro.so)."""
+    _link(MICRO_LIB, MICRO_SOURCES, verbose)
+    return _link(LIB, SOURCES, verbose)
 
 
 if __name__ == "__main__":

@@ -1,0 +1,318 @@
+// attn_micro.hip -- microbenchmarks of the gfx950 issue rates that the
+// attention kernels' design rests on (libattn_micro.so; not part of the
+// attention ABI in include/attn.h).
+//
+// The FlashAttention-4 section of "FlashAttention 1-4 evolution cheat sheet"
+// (argus-lessons) prices one forward tile by counting cycles per unit: matrix
+// work, exponentials, shared-memory reads.  These kernels measure the gfx950
+// numbers for the same count, in shader-clock cycles read from the wave's own
+// counter (s_memtime), so the results do not depend on the clock the chip
+// runs at; the clock itself is measured beside them (s_memtime cycles against
+// the constant-rate s_memrealtime counter).
+//
+//   rate:  one kind of VALU instruction on 16 independent chains per lane (or
+//          one dependent chain), w waves per SIMD: cycles per instruction per
+//          SIMD (throughput) or per dependent instruction (latency).
+//   mix:   32x32x16 bf16 MFMAs on four independent accumulators, each
+//          followed by k FMAs and e exponentials (v_exp_f32, or exp2_poly)
+//          on independent chains, interleaved by sched_group_barrier as the
+//          attention kernel interleaves its step: cycles per MFMA per SIMD.
+//
+// Occupancy is pinned: one workgroup per CU (96 KB of LDS each) of 4 w waves,
+// so every SIMD holds exactly w waves.  256 workgroups fill the 256 CUs.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_common.h"
+#include "exp2_poly.h"
+
+namespace attn_gfx950 {
+namespace micro {
+
+constexpr int kLdsBytes = 96 * 1024;  // > 160 KB / 2: one workgroup per CU
+constexpr int kChains = 16;
+
+enum Op { kOpFma = 0, kOpExp = 1, kOpPoly = 2, kOpMul = 3 };
+
+template <int OP>
+__device__ __forceinline__ float apply(float x)
+{
+    if constexpr (OP == kOpFma)
+        return __builtin_fmaf(x, 0.999f, 0.001f);
+    else if constexpr (OP == kOpExp)
+        return __builtin_amdgcn_exp2f(-x);  // neg is an input modifier: one instruction
+    else if constexpr (OP == kOpPoly)
+        return exp2_poly(-x);
+    else
+        return x * 0.999f;
+}
+
+// Each wave stores its own start and end stamps (shader cycles and real-time
+// ticks); the host takes a workgroup's span as the latest end minus the
+// earliest start, since the waves sharing a SIMD need not finish together.
+__device__ __forceinline__ void record(unsigned long long *times, uint64_t c0, uint64_t r0)
+{
+    const uint64_t c1 = __builtin_amdgcn_s_memtime();
+    const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+    const int wave = threadIdx.x / kWave;
+    if ((threadIdx.x & (kWave - 1)) == 0) {
+        const size_t i = ((size_t)blockIdx.x * (blockDim.x / kWave) + wave) * 4;
+        times[i] = c0;
+        times[i + 1] = c1;
+        times[i + 2] = r0;
+        times[i + 3] = r1;
+    }
+}
+
+// DEP = false: 16 independent chains, 16 instructions per iteration.
+// DEP = true: one chain, 16 dependent instructions per iteration.
+template <int OP, bool DEP>
+__global__ __launch_bounds__(1024) void rate_kernel(float *sink, unsigned long long *times, int iters)
+{
+    extern __shared__ char lds_pin[];
+    float x[kChains];
+#pragma unroll
+    for (int i = 0; i < kChains; ++i)
+        x[i] = 0.25f + 0.001f * (float)((threadIdx.x + i) & 63);
+    if (threadIdx.x == 0)
+        lds_pin[0] = 0;
+    __syncthreads();
+    const uint64_t c0 = __builtin_amdgcn_s_memtime();
+    const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+    for (int it = 0; it < iters; ++it) {
+        if constexpr (DEP) {
+#pragma unroll
+            for (int i = 0; i < kChains; ++i)
+                x[0] = apply<OP>(x[0]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kChains; ++i)
+                x[i] = apply<OP>(x[i]);
+        }
+        asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]),
+                     "+v"(x[7]), "+v"(x[8]), "+v"(x[9]), "+v"(x[10]), "+v"(x[11]), "+v"(x[12]), "+v"(x[13]),
+                     "+v"(x[14]), "+v"(x[15]));
+    }
+    record(times, c0, r0);
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < kChains; ++i)
+        s += x[i];
+    sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s + (float)lds_pin[threadIdx.x & 7];
+}
+
+// Four MFMAs per iteration on independent accumulators; after each, K FMAs
+// and E exponentials (POLY: exp2_poly) on the 16 independent chains.
+template <int K, int E, bool POLY>
+__global__ __launch_bounds__(1024) void mix_kernel(float *sink, unsigned long long *times, int iters)
+{
+    extern __shared__ char lds_pin[];
+    const int t = threadIdx.x;
+    bf16x8 a, b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        a[i] = (__bf16)(0.001f * (float)((t + i) & 63));
+        b[i] = (__bf16)(0.002f * (float)((t + 3 * i) & 63));
+    }
+    f32x16 acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        acc[j] = f32x16{};
+    float x[kChains];
+#pragma unroll
+    for (int i = 0; i < kChains; ++i)
+        x[i] = 0.25f + 0.001f * (float)((t + i) & 63);
+    if (t == 0)
+        lds_pin[0] = 0;
+    __syncthreads();
+    const uint64_t c0 = __builtin_amdgcn_s_memtime();
+    const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+                x[(j * (K + E) + k) % kChains] = apply<kOpFma>(x[(j * (K + E) + k) % kChains]);
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                x[(j * (K + E) + K + e) % kChains] =
+                    apply<POLY ? kOpPoly : kOpExp>(x[(j * (K + E) + K + e) % kChains]);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x402, K + E * (POLY ? 9 : 1), 0);  // VALU incl. transcendental (exp2_poly of -x: 9)
+        }
+    }
+    record(times, c0, r0);
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            s += acc[j][i];
+#pragma unroll
+    for (int i = 0; i < kChains; ++i)
+        s += x[i];
+    sink[(size_t)blockIdx.x * blockDim.x + t] = s + (float)lds_pin[t & 7];
+}
+
+template <typename F>
+static int run(F kernel, int waves_per_simd, int iters, double *cycles, double *clock_ghz, double *ms)
+{
+    if (waves_per_simd < 1 || waves_per_simd > 4 || iters < 1)
+        return 2;
+    const int grid = 256, block = 4 * waves_per_simd * kWave, waves = grid * block / kWave;
+    float *sink = nullptr;
+    unsigned long long *times = nullptr;
+    if (hipMalloc(&sink, (size_t)grid * block * sizeof(float)) != hipSuccess)
+        return 7;
+    if (hipMalloc(&times, (size_t)waves * 4 * sizeof(unsigned long long)) != hipSuccess) {
+        (void)hipFree(sink);
+        return 7;
+    }
+    int rate_khz = 0;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    (void)hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, dev);
+    hipEvent_t e0, e1;
+    (void)hipEventCreate(&e0);
+    (void)hipEventCreate(&e1);
+    int status = 0;
+    for (int rep = 0; rep < 3 && status == 0; ++rep) {  // the last of three launches is kept
+        (void)hipEventRecord(e0, nullptr);
+        hipLaunchKernelGGL(kernel, dim3(grid), dim3(block), kLdsBytes, nullptr, sink, times, iters);
+        (void)hipEventRecord(e1, nullptr);
+        if (hipGetLastError() != hipSuccess || hipEventSynchronize(e1) != hipSuccess)
+            status = 7;
+    }
+    if (status == 0) {
+        float t = 0.f;
+        (void)hipEventElapsedTime(&t, e0, e1);
+        unsigned long long *h = new unsigned long long[(size_t)waves * 4];
+        if (hipMemcpy(h, times, (size_t)waves * 4 * sizeof(unsigned long long), hipMemcpyDeviceToHost) != hipSuccess)
+            status = 7;
+        const int per = block / kWave;
+        double c = 0.0, r = 0.0;
+        for (int g = 0; g < grid; ++g) {  // span of each workgroup: earliest start to latest end
+            unsigned long long c_lo = ~0ull, c_hi = 0, r_lo = ~0ull, r_hi = 0;
+            for (int w = 0; w < per; ++w) {
+                const unsigned long long *e = h + ((size_t)g * per + w) * 4;
+                c_lo = e[0] < c_lo ? e[0] : c_lo;
+                c_hi = e[1] > c_hi ? e[1] : c_hi;
+                r_lo = e[2] < r_lo ? e[2] : r_lo;
+                r_hi = e[3] > r_hi ? e[3] : r_hi;
+            }
+            c += (double)(c_hi - c_lo);
+            r += (double)(r_hi - r_lo);
+        }
+        delete[] h;
+        c /= grid;
+        r /= grid;
+        *cycles = c;  // mean over workgroups of the shader cycles one workgroup's timed loops span
+        *clock_ghz = rate_khz > 0 && r > 0 ? c / (r / (rate_khz * 1e3)) / 1e9 : 0.0;
+        *ms = t;
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    (void)hipFree(sink);
+    (void)hipFree(times);
+    return status;
+}
+
+// Elementwise exp2_poly and v_exp_f32 of n inputs (accuracy tests).
+__global__ __launch_bounds__(256) void exp2_eval_kernel(const float *x, float *poly, float *hw, int n)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) {
+        poly[i] = exp2_poly(x[i]);
+        hw[i] = __builtin_amdgcn_exp2f(x[i]);
+    }
+}
+
+}  // namespace micro
+}  // namespace attn_gfx950
+
+using namespace attn_gfx950::micro;
+
+// One rate measurement: op (0 fma, 1 v_exp_f32, 2 exp2_poly, 3 mul),
+// dependent (0: 16 independent chains, 1: one chain), waves per SIMD 1..4.
+// out[0] = cycles per instruction per SIMD (independent: the SIMD's
+// throughput over all its waves) or per dependent instruction (latency);
+// out[1] = shader clock in GHz; out[2] = launch time in ms.  Returns 0, 2
+// for arguments outside the table, 7 for a HIP error.
+extern "C" __attribute__((visibility("default"))) int attn_micro_rate(int op, int dependent, int waves_per_simd,
+                                                                      int iters, double *out)
+{
+    double cyc = 0, ghz = 0, ms = 0;
+    int st = 2;
+#define ATTN_MICRO_RATE(O)                                                                                  \
+    if (op == O)                                                                                            \
+        st = dependent ? run(rate_kernel<O, true>, waves_per_simd, iters, &cyc, &ghz, &ms)                   \
+                       : run(rate_kernel<O, false>, waves_per_simd, iters, &cyc, &ghz, &ms);
+    ATTN_MICRO_RATE(kOpFma)
+    ATTN_MICRO_RATE(kOpExp)
+    ATTN_MICRO_RATE(kOpPoly)
+    ATTN_MICRO_RATE(kOpMul)
+#undef ATTN_MICRO_RATE
+    if (st != 0)
+        return st;
+    const double insts = (double)iters * kChains;
+    out[0] = dependent ? cyc / insts : cyc / (insts * waves_per_simd);
+    out[1] = ghz;
+    out[2] = ms;
+    return 0;
+}
+
+// One mix measurement: after each 32x32x16 bf16 MFMA, k_fma FMAs and n_exp
+// exponentials (poly: exp2_poly instead of v_exp_f32).  Instances:
+// (k, e) in (0,0) (2,1) (3,1) (4,1) (5,1) (6,1) (4,2) (8,0), and poly with
+// (3,1) (4,1).  out[0] = cycles per MFMA per SIMD (32 = the matrix core's
+// own rate for this shape), out[1] = shader clock (GHz), out[2] = ms,
+// out[3] = whole-chip bf16 TFLOP/s of the MFMAs.
+extern "C" __attribute__((visibility("default"))) int attn_micro_mix(int k_fma, int n_exp, int poly,
+                                                                     int waves_per_simd, int iters, double *out)
+{
+    double cyc = 0, ghz = 0, ms = 0;
+    int st = 2;
+#define ATTN_MICRO_MIX(K, E, P)                                                                 \
+    if (k_fma == K && n_exp == E && (poly != 0) == P)                                           \
+        st = run(mix_kernel<K, E, P>, waves_per_simd, iters, &cyc, &ghz, &ms);
+    ATTN_MICRO_MIX(0, 0, false)
+    ATTN_MICRO_MIX(2, 1, false)
+    ATTN_MICRO_MIX(3, 1, false)
+    ATTN_MICRO_MIX(4, 1, false)
+    ATTN_MICRO_MIX(5, 1, false)
+    ATTN_MICRO_MIX(6, 1, false)
+    ATTN_MICRO_MIX(4, 2, false)
+    ATTN_MICRO_MIX(8, 0, false)
+    ATTN_MICRO_MIX(3, 1, true)
+    ATTN_MICRO_MIX(4, 1, true)
+#undef ATTN_MICRO_MIX
+    if (st != 0)
+        return st;
+    const double mfmas = (double)iters * 4;
+    out[0] = cyc / (mfmas * waves_per_simd);
+    out[1] = ghz;
+    out[2] = ms;
+    out[3] = 256.0 * 4 * waves_per_simd * mfmas * 32768.0 / (ms * 1e-3) / 1e12;
+    return 0;
+}
+
+// poly[i] = exp2_poly(x[i]) and hw[i] = v_exp_f32(x[i]) for i < n; x, poly
+// and hw are device arrays of n floats.  One kernel on `stream` (a
+// hipStream_t as void*).  Returns 0, 2 for n < 0 or a null pointer, 7 for a
+// launch error.
+extern "C" __attribute__((visibility("default"))) int attn_micro_exp2(const float *x, float *poly, float *hw, int n,
+                                                                      void *stream)
+{
+    if (n < 0 || (n > 0 && (!x || !poly || !hw)))
+        return 2;
+    if (n == 0)
+        return 0;
+    hipLaunchKernelGGL(exp2_eval_kernel, dim3((n + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream), x,
+                       poly, hw, n);
+    return hipGetLastError() == hipSuccess ? 0 : 7;
+}

@@ -1,0 +1,75 @@
+"""ctypes binding of libattn_micro.so: the gfx950 issue-rate microbenchmarks
+(csrc/attn_micro.hip) and the exp2_poly accuracy kernel.  Measurement tools,
+not part of the attention ABI.  Raises if the library is not built."""
+
+import ctypes
+import os
+
+import torch  # noqa: F401  (loaded first: one HIP runtime per process)
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn_micro.so")
+OPS = {"fma": 0, "exp": 1, "poly": 2, "mul": 3}
+# VALU instructions per loop element of each rate op: exp2_poly applied to -x
+# is the negation plus its 8 instructions; v_exp_f32 takes the negation as an
+# input modifier.
+INSTS_PER_OP = {"fma": 1, "exp": 1, "poly": 9, "mul": 1}
+MIXES = [(0, 0, False), (2, 1, False), (3, 1, False), (4, 1, False), (5, 1, False), (6, 1, False),
+         (4, 2, False), (8, 0, False), (3, 1, True), (4, 1, True)]
+
+_lib = None
+
+
+def load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise FileNotFoundError("libattn_micro.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    d4 = ctypes.POINTER(ctypes.c_double)
+    lib.attn_micro_rate.restype = ctypes.c_int
+    lib.attn_micro_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, d4]
+    lib.attn_micro_mix.restype = ctypes.c_int
+    lib.attn_micro_mix.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, d4]
+    lib.attn_micro_exp2.restype = ctypes.c_int
+    lib.attn_micro_exp2.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                    ctypes.c_void_p]
+    _lib = lib
+    return lib
+
+
+def rate(op, waves_per_simd, dependent=False, iters=20000):
+    """Cycles per instruction of one VALU op kind: per SIMD over all its waves
+    (independent chains) or per dependent instruction (one chain); and the
+    measured shader clock (GHz)."""
+    out = (ctypes.c_double * 4)()
+    st = load().attn_micro_rate(OPS[op], 1 if dependent else 0, waves_per_simd, iters, out)
+    if st:
+        raise RuntimeError("attn_micro_rate status %d" % st)
+    return {"op": op, "waves_per_simd": waves_per_simd, "dependent": dependent,
+            "cycles_per_element": out[0], "cycles_per_inst": out[0] / INSTS_PER_OP[op],
+            "clock_ghz": out[1], "ms": out[2]}
+
+
+def mix(k_fma, n_exp, poly, waves_per_simd, iters=20000):
+    """Cycles per 32x32x16 bf16 MFMA per SIMD with k_fma FMAs and n_exp
+    exponentials after each MFMA (32 = the matrix core's own rate)."""
+    out = (ctypes.c_double * 4)()
+    st = load().attn_micro_mix(k_fma, n_exp, 1 if poly else 0, waves_per_simd, iters, out)
+    if st:
+        raise RuntimeError("attn_micro_mix status %d" % st)
+    return {"k_fma": k_fma, "n_exp": n_exp, "exp": "exp2_poly" if poly else "v_exp_f32",
+            "waves_per_simd": waves_per_simd, "cycles_per_mfma": out[0], "clock_ghz": out[1],
+            "ms": out[2], "tflops": out[3]}
+
+
+def exp2(x, stream=None):
+    """(exp2_poly(x), v_exp_f32(x)) elementwise for a contiguous fp32 CUDA tensor."""
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous float32 CUDA tensor")
+    poly, hw = torch.empty_like(x), torch.empty_like(x)
+    s = stream.cuda_stream if stream is not None else torch.cuda.current_stream(x.device).cuda_stream
+    st = load().attn_micro_exp2(x.data_ptr(), poly.data_ptr(), hw.data_ptr(), x.numel(), s)
+    if st:
+        raise RuntimeError("attn_micro_exp2 status %d" % st)
+    return poly, hw
