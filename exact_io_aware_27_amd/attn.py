@@ -21,8 +21,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so"
 ATTN_OK = 0
 STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_NULL_PTR", 2: "ATTN_BAD_SHAPE", 3: "ATTN_UNSUPPORTED_D",
                 4: "ATTN_BAD_SCALE", 5: "ATTN_MISALIGNED", 6: "ATTN_ALIAS", 7: "ATTN_HIP",
-                8: "ATTN_BAD_WORKSPACE", 9: "ATTN_BAD_ARGUMENT"}
-EXPORTS = ("attn_fwd", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_bytes", "attn_bwd",
+                8: "ATTN_BAD_WORKSPACE", 9: "ATTN_BAD_ARGUMENT", 10: "ATTN_SCRATCH_TOO_SMALL"}
+EXPORTS = ("attn_fwd", "attn_fwd_splitkv", "attn_fwd_splitkv_noalloc", "attn_noalloc_scratch_bytes",
+           "attn_fwd_splitkv_workspace_bytes", "attn_bwd",
            "attn_bwd_workspace_bytes", "attn_fp8_padded_rows", "attn_fp8_quantize", "attn_fwd_fp8",
            "attn_status_string", "attn_last_hip_error")
 
@@ -55,6 +56,11 @@ def load():
     lib.attn_fwd_splitkv.restype = ctypes.c_int
     lib.attn_fwd_splitkv.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float,
                                      i64, p, i64, p]
+    lib.attn_fwd_splitkv_noalloc.restype = ctypes.c_int
+    lib.attn_fwd_splitkv_noalloc.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, ctypes.c_int,
+                                             ctypes.c_float, i64, p]
+    lib.attn_noalloc_scratch_bytes.restype = i64
+    lib.attn_noalloc_scratch_bytes.argtypes = []
     lib.attn_fwd_splitkv_workspace_bytes.restype = i64
     lib.attn_fwd_splitkv_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
     lib.attn_bwd.restype = ctypes.c_int
@@ -173,6 +179,33 @@ def attn_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, num_splits
     """attn_fwd_splitkv of include/attn.h; raises AttnError on a nonzero status."""
     st = attn_fwd_splitkv_status(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, num_splits,
                                  workspace, workspace_bytes, stream)
+    if st != ATTN_OK:
+        raise AttnError(st, load().attn_last_hip_error() if st == 7 else 0)
+
+
+def noalloc_scratch_bytes():
+    """attn_noalloc_scratch_bytes of include/attn.h: the per-GPU scratch size."""
+    return load().attn_noalloc_scratch_bytes()
+
+
+def attn_fwd_splitkv_noalloc_status(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, num_splits, stream=None):
+    """Call attn_fwd_splitkv_noalloc and return its status code (0 = ATTN_OK).
+    Arguments as attn_fwd_splitkv_status, without the workspace."""
+    qs, ks = (int(B), int(H), int(Nq), int(d)), (int(B), int(H), int(Nk), int(d))
+    _check(q, "q", qs, torch.bfloat16)
+    _check(o, "o", qs, torch.bfloat16)
+    _check(k, "k", ks, torch.bfloat16)
+    _check(v, "v", ks, torch.bfloat16)
+    _check(lse, "lse", qs[:3], torch.float32)
+    lib = load()
+    return lib.attn_fwd_splitkv_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(Nq),
+                                        int(Nk), int(d), 1 if causal else 0, float(scale), int(num_splits),
+                                        _stream(stream))
+
+
+def attn_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, num_splits, stream=None):
+    """attn_fwd_splitkv_noalloc of include/attn.h; raises AttnError on a nonzero status."""
+    st = attn_fwd_splitkv_noalloc_status(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, num_splits, stream)
     if st != ATTN_OK:
         raise AttnError(st, load().attn_last_hip_error() if st == 7 else 0)
 

@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/attn.h"
 #include "attn_launch.h"
@@ -45,6 +46,7 @@ extern "C" const char *attn_status_string(int status)
     case ATTN_HIP: return "ATTN_HIP";
     case ATTN_BAD_WORKSPACE: return "ATTN_BAD_WORKSPACE";
     case ATTN_BAD_ARGUMENT: return "ATTN_BAD_ARGUMENT";
+    case ATTN_SCRATCH_TOO_SMALL: return "ATTN_SCRATCH_TOO_SMALL";
     default: return "ATTN_UNKNOWN_STATUS";
     }
 }
@@ -53,11 +55,54 @@ extern "C" int attn_last_hip_error(void) { return g_last_hip_error; }
 
 namespace {
 
-// Shared validation and launch of attn_fwd and attn_fwd_splitkv, in the
-// documented order.
+// The scratch of attn_fwd_splitkv_noalloc: one array per GPU the library
+// runs on (each device holds its own copy at its own address), kept until the
+// process ends.  Host code never uses the array's name as an address: the
+// name is a host-side stand-in, and a kernel handed it would fault.  Each
+// device's address is looked up once with hipGetSymbolAddress and kept in
+// g_scratch.
+constexpr int64_t kScratchBytes = int64_t(32) << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+// Device address of the current device's scratch array; looked up on the
+// first call on each device (with that device current).
+hipError_t scratch_address(void **out)
+{
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess)
+        return err;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch[dev] == nullptr) {
+        void *p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess)
+            return err;
+        if (p == nullptr)
+            return hipErrorInvalidSymbol;
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return hipSuccess;
+}
+
+// Shared validation and launch of attn_fwd, attn_fwd_splitkv and
+// attn_fwd_splitkv_noalloc, in the documented order.  use_scratch: the
+// workspace arguments are ignored and the per-range partials go to the
+// library's scratch array.
 int fwd_common(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B, int64_t H,
                int64_t Nq, int64_t Nk, int64_t d, int causal, float scale, int64_t num_splits,
-               void *workspace, int64_t workspace_bytes, void *stream)
+               void *workspace, int64_t workspace_bytes, void *stream, bool use_scratch = false)
 {
     // 1. Shapes: non-negative, byte sizes and index ranges representable.
     int64_t BH, qrows, krows, qelems, kelems, qbytes, kbytes, lse_bytes;
@@ -105,8 +150,16 @@ int fwd_common(const void *q, const void *k, const void *v, void *o, float *lse,
     if (lse && (overlaps(lse, lse_bytes, q, qbytes) || overlaps(lse, lse_bytes, k, kbytes) ||
                 overlaps(lse, lse_bytes, v, kbytes) || overlaps(lse, lse_bytes, o, qbytes)))
         return ATTN_ALIAS;
-    // 8. Workspace (split ranges only).
-    if (splits > 1) {
+    // 8. Workspace (split ranges only): the caller's, or the library's scratch.
+    if (splits > 1 && use_scratch) {
+        if (ws_need > kScratchBytes)
+            return ATTN_SCRATCH_TOO_SMALL;
+        const hipError_t err = scratch_address(&workspace);
+        if (err != hipSuccess) {
+            g_last_hip_error = static_cast<int>(err);
+            return ATTN_HIP;
+        }
+    } else if (splits > 1) {
         if (!workspace || mis16(workspace) || workspace_bytes < ws_need ||
             overlaps(workspace, ws_need, q, qbytes) || overlaps(workspace, ws_need, k, kbytes) ||
             overlaps(workspace, ws_need, v, kbytes) || overlaps(workspace, ws_need, o, qbytes) ||
@@ -154,6 +207,15 @@ extern "C" int attn_fwd_splitkv(const void *q, const void *k, const void *v, voi
     return fwd_common(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, num_splits, workspace,
                       workspace_bytes, stream);
 }
+
+extern "C" int attn_fwd_splitkv_noalloc(const void *q, const void *k, const void *v, void *o, float *lse,
+                                        int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                                        float scale, int64_t num_splits, void *stream)
+{
+    return fwd_common(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, num_splits, nullptr, 0, stream, true);
+}
+
+extern "C" int64_t attn_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 extern "C" int64_t attn_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t d,
                                                     int64_t num_splits)

@@ -60,7 +60,9 @@ enum attn_status {
     ATTN_BAD_WORKSPACE = 8, /* attn_fwd_splitkv, attn_bwd: workspace NULL, not 16-byte
                                aligned, smaller than the *_workspace_bytes() size, or
                                overlapping a tensor of the call */
-    ATTN_BAD_ARGUMENT = 9   /* attn_fp8_quantize: signs given with the transposed layout */
+    ATTN_BAD_ARGUMENT = 9,  /* attn_fp8_quantize: signs given with the transposed layout */
+    ATTN_SCRATCH_TOO_SMALL = 10 /* attn_fwd_splitkv_noalloc: the call needs more than
+                                   attn_noalloc_scratch_bytes() of scratch */
 };
 
 /*
@@ -127,6 +129,38 @@ ATTN_API int attn_fwd_splitkv(const void *q, const void *k, const void *v, void 
                      int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
                      int causal, float scale, int64_t num_splits,
                      void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * attn_fwd_splitkv_noalloc -- attn_fwd_splitkv for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same arguments and result, without
+ * the workspace arguments.  The per-range partials go to scratch memory the
+ * library holds: one file-scope device array of attn_noalloc_scratch_bytes()
+ * bytes on each GPU the library runs on, kept until the process ends.  The
+ * call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine).  Its first call on a device looks up that device's copy of the
+ * array (hipGetSymbolAddress, with that device current), so call it with
+ * the current device set to the one `stream` belongs to.
+ *
+ * Every call on one GPU shares that GPU's array, whose contents are left as
+ * the last call wrote them: calls that overlap in time on one GPU (other
+ * streams, other threads) race and must be serialised by the caller.  Every
+ * element a call reads back was written earlier in the same call, so nothing
+ * needs clearing between calls.
+ *
+ * Errors: as attn_fwd_splitkv up to ALIAS (BAD_SHAPE, UNSUPPORTED_D,
+ * BAD_SCALE, empty -> OK, NULL_PTR, MISALIGNED, ALIAS), then
+ * ATTN_SCRATCH_TOO_SMALL when attn_fwd_splitkv_workspace_bytes() of the
+ * call exceeds attn_noalloc_scratch_bytes() (no HIP call is made), then
+ * ATTN_HIP (the lookup or the launch failed).  When one key range results
+ * the scratch is not used.
+ */
+ATTN_API int attn_fwd_splitkv_noalloc(const void *q, const void *k, const void *v, void *o, float *lse,
+                             int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                             int causal, float scale, int64_t num_splits, void *stream);
+
+/* Size in bytes of attn_fwd_splitkv_noalloc's scratch array (per GPU). */
+ATTN_API int64_t attn_noalloc_scratch_bytes(void);
 
 /* Bytes of workspace attn_fwd_splitkv needs (0 for num_splits == 1);
  * -1 if the arguments are invalid (negative, d not 64/128, num_splits < 1,

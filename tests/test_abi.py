@@ -30,6 +30,7 @@ def _declared():
 
 def test_header_declares_the_abi():
     assert set(_declared()) == {"attn_fwd", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_bytes",
+                                "attn_fwd_splitkv_noalloc", "attn_noalloc_scratch_bytes",
                                 "attn_bwd", "attn_bwd_workspace_bytes", "attn_fp8_padded_rows",
                                 "attn_fp8_quantize", "attn_fwd_fp8", "attn_status_string",
                                 "attn_last_hip_error"}
@@ -47,7 +48,7 @@ def test_library_exports_every_declared_symbol(lib):
 def test_status_strings(lib):
     names = ["ATTN_OK", "ATTN_NULL_PTR", "ATTN_BAD_SHAPE", "ATTN_UNSUPPORTED_D",
              "ATTN_BAD_SCALE", "ATTN_MISALIGNED", "ATTN_ALIAS", "ATTN_HIP", "ATTN_BAD_WORKSPACE",
-             "ATTN_BAD_ARGUMENT"]
+             "ATTN_BAD_ARGUMENT", "ATTN_SCRATCH_TOO_SMALL"]
     for code, name in enumerate(names):
         assert lib.attn_status_string(code).decode() == name
     assert lib.attn_status_string(99).decode() == "ATTN_UNKNOWN_STATUS"
@@ -116,6 +117,31 @@ def test_splitkv_argument_errors_before_any_hip_call(lib, kw, status):
 def test_splitkv_causal_needs_no_more_queries_than_keys_only_under_the_mask(lib):
     # non-causal Nq > Nk passes the shape checks and stops at the misaligned output
     assert _split(lib, Nq=1001, Nk=1000, causal=0, o=O + 4) == 5
+
+
+def _noalloc(lib, q=Q, k=K, v=V, o=O, lse=L, B=2, H=3, Nq=7, Nk=1000, d=128, causal=1, scale=0.1, S=4):
+    return lib.attn_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, S, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Nq=-1), 2), (dict(S=0), 2), (dict(Nk=0), 2), (dict(Nq=1001, Nk=1000), 2),
+    (dict(d=96), 3), (dict(scale=float("inf")), 4),
+    (dict(Nq=0, q=None, o=None), 0), (dict(H=0), 0),
+    (dict(v=None), 1), (dict(o=O + 8), 5), (dict(o=V + 64), 6), (dict(lse=O), 6),
+    # the partials of 64 x 32 heads x 128 queries in 8 ranges (1.08 GB) exceed the scratch
+    (dict(B=64, H=32, Nq=128, S=8, q=1 << 32, k=2 << 32, v=3 << 32, o=4 << 32, lse=5 << 32), 10),
+    # a bad shape is reported before the scratch size
+    (dict(B=64, H=32, Nq=128, S=8, d=96), 3),
+])
+def test_noalloc_argument_errors_before_any_hip_call(lib, kw, status):
+    assert _noalloc(lib, **kw) == status
+
+
+def test_noalloc_scratch_bytes(lib):
+    assert lib.attn_noalloc_scratch_bytes() == 32 << 20
+    # the largest split call the scratch serves is the one whose workspace fits
+    ws = lib.attn_fwd_splitkv_workspace_bytes(2, 3, 7, 128, 4)
+    assert 0 < ws <= lib.attn_noalloc_scratch_bytes()
 
 
 def test_splitkv_workspace_bytes(lib):
