@@ -11,6 +11,11 @@ literal on the five workloads; on the extra edge cases (a handful of keys,
 where |O| stays near 1 and a single correct bf16 rounding of the exact O
 already averages ~1e-3) it is mean|dO| <= 1e-3 + mean rounding floor.  The
 rounding floor, |bf16(O_ref) - O_ref|, depends on the oracle alone.
+
+Where |O| keeps that floor below the bar (every workload but the large-logit
+one, whose |O| reaches 4..8) the max check is also asserted literally,
+max|dO| <= 1e-2 (assert_parity(..., literal_max=True)); the report always
+carries the literal figures beside the floor.
 """
 
 import numpy as np
@@ -52,9 +57,11 @@ def compare(o_gpu, lse_gpu, o_ref, lse_ref):
     return rep
 
 
-def assert_parity(rep, what="", literal_mean=False):
+def assert_parity(rep, what="", literal_mean=False, literal_max=False):
     assert rep["finite"], "%s: non-finite output %s" % (what, rep)
     assert rep["n_over"] == 0, "%s: max|dO| over 1e-2 + half-ulp bound: %s" % (what, rep)
+    if literal_max:
+        assert rep["max_abs"] <= MAX_ABS, "%s: max|dO| over the literal 1e-2: %s" % (what, rep)
     mean_bound = MEAN_ABS if literal_mean else MEAN_ABS + rep["floor_mean"]
     assert rep["mean_abs"] <= mean_bound, "%s: mean|dO| %s" % (what, rep)
     if "lse_max_abs" in rep:

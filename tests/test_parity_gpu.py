@@ -37,13 +37,13 @@ def run(q, k, v, causal, scale, with_lse=True, stream=None):
     return o, lse
 
 
-def check_full(q, k, v, causal, scale, what, literal_mean=False):
+def check_full(q, k, v, causal, scale, what, literal_mean=False, literal_max=False):
     say("case:", what, tuple(q.shape), "causal" if causal else "non-causal")
     o, lse = run(q, k, v, causal, scale)
     o_ref, lse_ref = oracle.attention(q, k, v, causal, scale)
     rep = parity.compare(o, lse, o_ref, lse_ref)
     say("  ", rep)
-    parity.assert_parity(rep, what, literal_mean=literal_mean)
+    parity.assert_parity(rep, what, literal_mean=literal_mean, literal_max=literal_max)
     return o, lse
 
 
@@ -59,16 +59,25 @@ def test_golden_closed_forms(case):
 def test_workload_tiny_all_rows():
     w = inputs.WORKLOADS[0]
     q, k, v = inputs.workload_qkv(w)
-    check_full(q, k, v, w.causal, w.scale, w.describe(), literal_mean=True)
+    check_full(q, k, v, w.causal, w.scale, w.describe(), literal_mean=True, literal_max=True)
 
 
 def test_workload_gpt2_small_all_rows():
     w = inputs.WORKLOADS[1]
     q, k, v = inputs.workload_qkv(w)
-    check_full(q, k, v, w.causal, w.scale, w.describe(), literal_mean=True)
+    check_full(q, k, v, w.causal, w.scale, w.describe(), literal_mean=True, literal_max=True)
 
 
-def _sampled(w, R, extra_rows=()):
+def test_workload_long_causal_all_rows():
+    """The headline workload (B=2 H=32 N=8192 d=128 causal) on every one of
+    its 524,288 query rows, in the launch configuration the bench times: the
+    literal bars (max|dO| <= 1e-2, mean|dO| <= 1e-3, |dLSE| <= 1e-3)."""
+    w = inputs.WORKLOADS[2]
+    q, k, v = inputs.workload_qkv(w)
+    check_full(q, k, v, w.causal, w.scale, w.describe(), literal_mean=True, literal_max=True)
+
+
+def _sampled(w, R, extra_rows=(), literal_max=False):
     say("case:", w.describe(), "rows/head", R)
     q, k, v = inputs.workload_qkv(w)
     o, lse = run(q, k, v, w.causal, w.scale)
@@ -77,23 +86,21 @@ def _sampled(w, R, extra_rows=()):
     o_ref, lse_ref = oracle.attention(q, k, v, w.causal, w.scale, rows=rows)
     rep = parity.compare(parity.gather_rows(o, rows), parity.gather_rows(lse, rows), o_ref, lse_ref)
     say("  ", rep)
-    parity.assert_parity(rep, w.describe(), literal_mean=True)
+    parity.assert_parity(rep, w.describe(), literal_mean=True, literal_max=literal_max)
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
 
 
-def test_workload_long_causal_sampled():
-    # Tile boundaries of the 128-row query tiles and 64-key tiles are always in.
-    _sampled(inputs.WORKLOADS[2], 240, extra_rows=(63, 64, 127, 128, 129, 4095, 4096, 8190))
-
-
 def test_workload_large_logits_sampled():
+    # |O| reaches 4..8 here, where one correct bf16 store is already up to
+    # 0.0156 off: the max check is 1e-2 plus half a bf16 ulp of |O| (the
+    # report prints the literal max beside the oracle-only floor).
     w = inputs.WORKLOADS[3]
     _sampled(w, w.rows_checked)
 
 
 def test_workload_very_long_causal_sampled():
     w = inputs.WORKLOADS[4]
-    _sampled(w, w.rows_checked)
+    _sampled(w, w.rows_checked, literal_max=True)
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -109,9 +116,10 @@ def test_ragged_lengths(N, d, causal):
 def test_growing_scores_move_the_reference(d, causal):
     """Large logits (Q, K ~ N(0, 4^2)) on keys whose norm grows along the
     sequence: each row's running max rises many times by more than the
-    kernel's slack, so the reference moves again and again (d = 128 decides
-    it from the next block's row max, d = 64 from each block's own sums and
-    takes the block's probabilities again)."""
+    kernel's slack, so the reference moves again and again (the non-causal
+    d = 128 instance decides it from the next block's row max; the causal
+    instances and d = 64 from each block's own sums, taking the block's
+    probabilities again)."""
     N = 1000
     q, k, v = inputs.make_qkv(1, 2, N, d, seed=3000 + d + causal, sigma_qk=4.0)
     ramp = torch.linspace(0.25, 2.0, N, dtype=torch.float32)[None, None, :, None]
