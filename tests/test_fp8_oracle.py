@@ -8,8 +8,12 @@
   quantize / dequant   -> E4M3's relative error bound per element
   attention_fp64       -> the pinned C oracle on bf16 inputs
   P-rounding noise     -> the actual E4M3 rounding of P, measured
+  tensor_quantize      -> a hand-worked tensor (exponent, codes, boundary)
+  attention_fp8        -> a hand-worked row whose P rounds to known E4M3 codes
   the pages' claim     -> block quantization with incoherent processing has
                           lower error than per-tensor FP8 on outlier-heavy input
+                          (direction only: the pages' 2.6x comes with no input
+                          distribution, so its size is parity unpinned)
 """
 
 import math
@@ -133,3 +137,53 @@ def test_block_and_incoherent_processing_beat_per_tensor_fp8_on_outliers():
           % (per_tensor, blocked, both, per_tensor / both))
     assert both < blocked <= per_tensor * 1.0001
     assert per_tensor / both > 1.5
+
+
+def test_tensor_quantize_closed_form():
+    """A hand-worked tensor.  amax = 1000: 448 * 2^1 = 896 < 1000 <= 448 * 2^2,
+    so E = 2 and the codes are x / 4 on the E4M3 grid: 250 lies in [128, 256)
+    where the quantum is 16, so it rounds to 256; 0.75, 0.125 and 1.75 are
+    exact; 2^-22 is below half the smallest subnormal (2^-9) and becomes 0.
+    An exponent off by one either way changes a code (E = 1 would need
+    500 > 448; E = 3 gives 125 -> 128)."""
+    x = np.array([[1000.0, -3.0, 0.5], [7.0, 0.0, 2.0 ** -20]])
+    codes, E = f8.tensor_quantize(x)
+    assert E == 2
+    np.testing.assert_array_equal(codes, [[256.0, -0.75, 0.125], [1.75, 0.0, 0.0]])
+    # the boundary: amax exactly 448 * 2^k takes E = k and code 448
+    codes, E = f8.tensor_quantize(np.array([[896.0, -1.0]]))
+    assert E == 1
+    np.testing.assert_array_equal(codes, [[448.0, -0.5]])
+    # all zeros: E = 0
+    codes, E = f8.tensor_quantize(np.zeros((2, 3)))
+    assert E == 0 and not codes.any()
+
+
+@pytest.mark.parametrize("shift", [0.0, 5.0, -7.25])
+def test_attention_fp8_closed_form(shift):
+    """One query against three keys with scores shift + (0, ln 0.3, ln 0.05):
+    P relative to the row max is (1, 0.3, 0.05), whose E4M3 roundings are
+    1, 0.3125 (quantum 2^-5 in [0.25, 0.5): 9.6 -> 10) and 0.05078125
+    (quantum 2^-8 in [2^-5, 2^-4): 12.8 -> 13).  O takes the rounded weights
+    over the unrounded sum 1.35, and LSE = shift + ln 1.35.  A P taken
+    against anything but the row max, a division by the rounded sum (1.3633)
+    or an LSE from it would each move the result."""
+    s = shift + np.array([0.0, math.log(0.3), math.log(0.05)])
+    d = 4
+    q = np.zeros((1, 1, 1, d))
+    q[..., 0] = 1.0
+    k = np.zeros((1, 1, 3, d))
+    k[0, 0, :, 0] = s
+    v = np.array([[[[1.0, 2.0, -1.0, 0.5], [-3.0, 0.25, 4.0, 1.0], [8.0, -8.0, 2.0, -2.0]]]])
+    prep = {"q": q, "k": k, "v": v, "qk_factor": 1.0}
+    o, lse = f8.attention_fp8(prep, False, 1.0)
+    w = np.array([1.0, 0.3125, 0.05078125])
+    np.testing.assert_allclose(o[0, 0, 0], (w @ v[0, 0]) / 1.35, rtol=1e-12)
+    assert abs(lse[0, 0, 0] - (shift + math.log(1.35))) <= 1e-12
+    # causal with Nq = 1 < Nk: the query is the last position and sees every key
+    o_c, lse_c = f8.attention_fp8(prep, True, 1.0)
+    np.testing.assert_array_equal(o_c, o)
+    # and with the rotation's factor: qk_factor d divides the scale back out
+    prep_r = dict(prep, k=k * 2.0, qk_factor=2.0)
+    o_r, _ = f8.attention_fp8(prep_r, False, 1.0)
+    np.testing.assert_allclose(o_r, o, rtol=1e-12)
