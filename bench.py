@@ -419,10 +419,8 @@ def bench_fp8(args):
     vt8, ve = attn.fp8_quantize(vd, transpose=True, stream=stream)
     od = torch.empty_like(qd)
     lsed = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
-    eff = w.scale / w.d  # the rotation multiplies Q K^T by d
-
     def attend():
-        attn.attn_fwd_fp8(q8, k8, vt8, qe, ke, ve, od, lsed, w.B, w.H, w.N, w.d, w.causal, eff, stream)
+        attn.attn_fwd_fp8(q8, k8, vt8, qe, ke, ve, od, lsed, w.B, w.H, w.N, w.d, w.causal, w.scale, True, stream)
 
     def quantize():
         attn.fp8_quantize_status(qd, w.B, w.H, w.N, w.d, False, signs, q8, qe, stream)

@@ -73,7 +73,8 @@ def load():
     lib.attn_fp8_quantize.restype = ctypes.c_int
     lib.attn_fp8_quantize.argtypes = [p, i64, i64, i64, i64, ctypes.c_int, p, p, p, p]
     lib.attn_fwd_fp8.restype = ctypes.c_int
-    lib.attn_fwd_fp8.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float, p]
+    lib.attn_fwd_fp8.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float,
+                                 ctypes.c_int, p]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_status_string.argtypes = [ctypes.c_int]
     lib.attn_last_hip_error.restype = ctypes.c_int
@@ -336,18 +337,19 @@ def fp8_quantize(x, transpose=False, signs=None, stream=None):
     return out, exps
 
 
-def attn_fwd_fp8_status(q8, k8, vt8, qe, ke, ve, o, lse, B, H, N, d, causal, scale, stream=None):
+def attn_fwd_fp8_status(q8, k8, vt8, qe, ke, ve, o, lse, B, H, N, d, causal, scale, rotated, stream=None):
     """Call attn_fwd_fp8 and return its status (0 = ATTN_OK)."""
     _check(o, "o", (int(B), int(H), int(N), int(d)), torch.bfloat16)
     _check(lse, "lse", (int(B), int(H), int(N)), torch.float32)
     lib = load()
     return lib.attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(vt8), _ptr(qe), _ptr(ke), _ptr(ve), _ptr(o), _ptr(lse),
-                            int(B), int(H), int(N), int(d), 1 if causal else 0, float(scale), _stream(stream))
+                            int(B), int(H), int(N), int(d), 1 if causal else 0, float(scale),
+                            1 if rotated else 0, _stream(stream))
 
 
-def attn_fwd_fp8(q8, k8, vt8, qe, ke, ve, o, lse, B, H, N, d, causal, scale, stream=None):
+def attn_fwd_fp8(q8, k8, vt8, qe, ke, ve, o, lse, B, H, N, d, causal, scale, rotated, stream=None):
     """attn_fwd_fp8 of include/attn.h; raises AttnError on a nonzero status."""
-    st = attn_fwd_fp8_status(q8, k8, vt8, qe, ke, ve, o, lse, B, H, N, d, causal, scale, stream)
+    st = attn_fwd_fp8_status(q8, k8, vt8, qe, ke, ve, o, lse, B, H, N, d, causal, scale, rotated, stream)
     if st != ATTN_OK:
         raise AttnError(st, load().attn_last_hip_error() if st == 7 else 0)
 
@@ -366,6 +368,5 @@ def attention_fp8(q, k, v, causal=False, scale=None, signs=None, stream=None):
     vt8, ve = fp8_quantize(v, transpose=True, stream=stream)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    eff = scale / d if signs is not None else scale  # the rotation multiplies Q K^T by d
-    attn_fwd_fp8(q8, k8, vt8, qe, ke, ve, o, lse, B, H, N, d, causal, eff, stream)
+    attn_fwd_fp8(q8, k8, vt8, qe, ke, ve, o, lse, B, H, N, d, causal, scale, signs is not None, stream)
     return o, lse

@@ -365,7 +365,7 @@ extern "C" int attn_fp8_quantize(const void *x, int64_t B, int64_t H, int64_t N,
 
 extern "C" int attn_fwd_fp8(const void *q8, const void *k8, const void *vt8, const void *q_exps, const void *k_exps,
                             const void *v_exps, void *o, float *lse, int64_t B, int64_t H, int64_t N, int64_t d,
-                            int causal, float scale, void *stream)
+                            int causal, float scale, int rotated, void *stream)
 {
     int64_t BH, rows, np_rows, bytes, obytes, lse_bytes, nexp;
     if (B < 0 || H < 0 || N < 0 || !mul_ok(B, H, &BH) || !mul_ok(BH, N, &rows))
@@ -406,7 +406,9 @@ extern "C" int attn_fwd_fp8(const void *q8, const void *k8, const void *vt8, con
     a.BH = BH;
     a.N = N;
     a.causal = causal != 0;
-    a.scale = scale;
+    // Q and K rotated by the same random-sign Hadamard matrix (+-1 entries,
+    // no 1/sqrt(d)) multiply their product by d: divide it out of the scale.
+    a.scale = rotated ? scale / static_cast<float>(d) : scale;
     a.stream = static_cast<hipStream_t>(stream);
     const hipError_t err = attn_fp8_launch(a);
     if (err != hipSuccess) {

@@ -241,7 +241,7 @@ ATTN_API int64_t attn_fp8_padded_rows(int64_t N);
  * rotated, x -> (x * s) H with H the 128 x 128 Sylvester Hadamard matrix
  * (+-1 entries, no 1/sqrt(128)), computed in fp32 by the fast transform with
  * strides 1, 2, ..., 64.  Q and K rotated with the same signs keep their
- * product times 128, so attn_fwd_fp8 then takes scale / 128.  Errors:
+ * product times 128; attn_fwd_fp8 with rotated != 0 divides it out.  Errors:
  * BAD_SHAPE, UNSUPPORTED_D (d != 128), BAD_ARGUMENT (signs with transpose),
  * (empty -> OK), NULL_PTR, MISALIGNED, ALIAS.  One kernel on `stream`.
  */
@@ -254,13 +254,17 @@ ATTN_API int attn_fp8_quantize(const void *x, int64_t B, int64_t H, int64_t N, i
  * produced (q8, k8 rows; vt8 transposed; their exponent arrays).  Both
  * products run on the FP8 matrix cores with the block scales applied by the
  * hardware; P is rounded to E4M3 for the P V product and O is divided by the
- * fp32 sum of the unrounded P.  causal, scale, stream as attn_fwd.  Errors as
- * attn_fwd (d != 128 is UNSUPPORTED_D); one kernel on `stream`.
+ * fp32 sum of the unrounded P.  scale is the softmax scale of the original
+ * (unrotated) Q and K, e.g. 1/sqrt(128).  rotated: nonzero when q8 and k8
+ * were quantized with the same sign_bits (incoherent processing): their
+ * product then carries the Hadamard factor 128, which the call divides out
+ * of scale itself.  causal, stream as attn_fwd.  Errors as attn_fwd
+ * (d != 128 is UNSUPPORTED_D); one kernel on `stream`.
  */
 ATTN_API int attn_fwd_fp8(const void *q8, const void *k8, const void *vt8, const void *q_exps,
                  const void *k_exps, const void *v_exps, void *o, float *lse,
                  int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
-                 void *stream);
+                 int rotated, void *stream);
 
 /* Static, human-readable name of a status code ("ATTN_OK", ...). */
 ATTN_API const char *attn_status_string(int status);

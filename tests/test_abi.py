@@ -199,8 +199,8 @@ def _quant(lib, x=Q, B=2, H=3, N=100, d=128, tr=0, signs=None, out=O, ex=L):
 
 
 def _fp8(lib, q=Q, k=K, v=V, qe=W, ke=W + 4096, ve=W + 8192, o=O, lse=L, B=2, H=3, N=100, d=128, causal=1,
-         scale=0.1):
-    return lib.attn_fwd_fp8(q, k, v, qe, ke, ve, o, lse, B, H, N, d, causal, scale, None)
+         scale=0.1, rotated=1):
+    return lib.attn_fwd_fp8(q, k, v, qe, ke, ve, o, lse, B, H, N, d, causal, scale, rotated, None)
 
 
 def test_fp8_argument_errors_before_any_hip_call(lib):

@@ -207,3 +207,30 @@ def test_non_positive_scale(scale):
     dl = np.abs(lse.double().cpu().numpy() - lse_ref)
     say("   mean z^2 %.3f, max |z| %.2f, max |dLSE| %.2e" % (np.mean(z ** 2), np.abs(z).max(), dl.max()))
     assert np.mean(z ** 2) <= 2.0 and np.abs(z).max() <= 6.0 and dl.max() <= 1e-3
+
+
+def test_rotated_flag_divides_the_scale_in_the_library():
+    """attn_fwd_fp8 takes the softmax scale of the original Q and K; with
+    rotated set the library divides the rotation's factor 128 out itself.
+    Through the C ABI: (scale, rotated) gives the same bits as (scale / 128,
+    not rotated), since dividing by a power of two is exact."""
+    from exact_io_aware_27_amd import attn
+    B, H, N, d = 1, 2, 300, 128
+    q, k, v = inputs.make_qkv(B, H, N, d, seed=4300)
+    signs = inputs.make_signs(d, seed=4301).numpy()
+    say("case: rotated flag", (B, H, N))
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    q8, qe = attn.fp8_quantize(qd, signs=signs)
+    k8, ke = attn.fp8_quantize(kd, signs=signs)
+    vt8, ve = attn.fp8_quantize(vd, transpose=True)
+    scale = d ** -0.5
+    outs = []
+    for sc, rot in ((scale, True), (scale / d, False)):
+        o = torch.empty_like(qd)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=DEV)
+        st = attn.attn_fwd_fp8_status(q8, k8, vt8, qe, ke, ve, o, lse, B, H, N, d, True, sc, rot,
+                                      torch.cuda.current_stream())
+        assert st == 0, st
+        outs.append((o, lse))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
