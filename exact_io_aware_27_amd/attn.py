@@ -16,7 +16,9 @@ import os
 
 import torch  # noqa: F401  (must be loaded first: see the module docstring)
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+# ATTN_LIB_PATH: another build of the same sources (the host-sanitizer build
+# of tests/sanitize_cpu.py); by default the in-tree library.
+LIB_PATH = os.environ.get("ATTN_LIB_PATH") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
 
 ATTN_OK = 0
 STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_NULL_PTR", 2: "ATTN_BAD_SHAPE", 3: "ATTN_UNSUPPORTED_D",

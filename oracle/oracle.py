@@ -17,9 +17,13 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "attn_oracle.c")
-_LIB = os.path.join(_HERE, "libattn_oracle.so")
 _BWD_SRC = os.path.join(_HERE, "attn_bwd_oracle.c")
-_BWD_LIB = os.path.join(_HERE, "libattn_bwd_oracle.so")
+# ATTN_ORACLE_LIB_DIR: a directory holding prebuilt libattn_oracle.so and
+# libattn_bwd_oracle.so of the same sources (the sanitizer build of
+# tests/sanitize_cpu.py); by default the libraries are built here.
+_PREBUILT = os.environ.get("ATTN_ORACLE_LIB_DIR")
+_LIB = os.path.join(_PREBUILT or _HERE, "libattn_oracle.so")
+_BWD_LIB = os.path.join(_PREBUILT or _HERE, "libattn_bwd_oracle.so")
 _lib = None
 _bwd_lib = None
 
@@ -31,6 +35,8 @@ def library_path():
 
 
 def _compile(src, lib, force):
+    if _PREBUILT:
+        return lib  # a prebuilt library of the same source is in use
     if not force and os.path.exists(lib) and os.path.getmtime(lib) >= os.path.getmtime(src):
         return lib
     tmp = lib + ".tmp%d" % os.getpid()
