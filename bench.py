@@ -29,7 +29,7 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "attn fwd TFLOP/s + % of bf16 MFMA peak, 1 GPU, N=8192 d=128 causal"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_long_causal_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_io_aware_27_amd", "csrc", f)
-                  for f in ("attn_fwd_kernel.hip", "attn_common.h")]  # the forward kernel's own code
+                  for f in ("attn_fwd_kernel.hip", "attn_common.h", "exp2_poly.h")]  # the forward kernel's own code
 
 
 def code_only(text):
@@ -539,6 +539,9 @@ def main():
     ap.add_argument("--parity", default=None, metavar="WORKLOADS",
                     help="parity report against the fp64 oracle: 'all' or comma-separated workload names; "
                          "one JSON line per workload (exit 3 if one fails its bar)")
+    ap.add_argument("--lib", default=None,
+                    help="load this build of the attention library instead of the in-tree one (A/B of build "
+                         "options, see exact_io_aware_27_amd/build.py --out)")
     ap.add_argument("--micro", action="store_true",
                     help="gfx950 issue-rate microbenchmarks (VALU, exp, exp2_poly, MFMA mixes) in shader cycles")
     ap.add_argument("--cpu-heads", type=int, default=1,
@@ -554,6 +557,10 @@ def main():
         print(json.dumps(pmc_summary(args.pmc_summary[0], args.pmc_summary[1],
                                      args.copy_calibration_mib or 1024)))
         return 0
+
+    if args.lib:
+        from exact_io_aware_27_amd import attn
+        attn.LIB_PATH = os.path.abspath(args.lib)
 
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
@@ -619,7 +626,7 @@ def main():
 
     tflops = w.flops / (ms * 1e-3) / 1e12
     compulsory = w.B * w.H * (8 * w.N * w.d + 4 * w.N)  # Q,K,V read + O write (bf16) + LSE (fp32)
-    traffic = measured_traffic()
+    traffic = measured_traffic() if not args.lib else None  # counters are of the in-tree build
     props = torch.cuda.get_device_properties(dev)
     out = {
         # the headline metric on its own workload; another workload names itself
@@ -654,7 +661,8 @@ def main():
                 "peak_GBps": HBM_PEAK_GBPS},
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "gcn_arch": getattr(props, "gcnArchName", None)},
-        "kernel_hash": kernel_hash(),
+        "kernel_hash": kernel_hash() if not args.lib else None,
+        "library": os.path.relpath(attn.LIB_PATH, ROOT),
         "context_other_hardware": {
             "FlashAttention-2, A100, TFLOP/s": 225, "FlashAttention-3 FP16 fwd, H100 SXM5, TFLOP/s": 740,
             "FlashAttention-4 BF16, B200, TFLOP/s": 1613},

@@ -23,10 +23,10 @@ FLAGS = [
 ]
 
 
-def _link(lib, sources, verbose):
+def _link(lib, sources, verbose, defines=()):
     srcs = [os.path.join(CSRC, s) for s in sources]
     tmp = lib + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + ["-o", tmp] + srcs
+    cmd = [HIPCC] + FLAGS + ["-D" + d for d in defines] + ["-o", tmp] + srcs
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
@@ -42,5 +42,23 @@ def build(verbose=False):
     return _link(LIB, SOURCES, verbose)
 
 
+def build_variant(out, defines, verbose=False):
+    """The attention library with build options (-D NAME=VALUE, e.g.
+    ATTN_EXP2_POLY_EVERY=4), written to `out`: for A/B measurements
+    (bench.py --lib out)."""
+    os.makedirs(os.path.dirname(os.path.abspath(out)), exist_ok=True)
+    return _link(os.path.abspath(out), SOURCES, verbose, defines)
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import argparse
+
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--define", action="append", default=[], metavar="NAME=VALUE",
+                    help="build option for a variant library (needs --out)")
+    ap.add_argument("--out", default=None, help="path of a variant library")
+    a = ap.parse_args()
+    if a.out:
+        print(build_variant(a.out, a.define, verbose=True))
+    else:
+        print(build(verbose=True))

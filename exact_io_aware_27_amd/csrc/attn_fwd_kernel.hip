@@ -75,6 +75,19 @@
 
 #include "attn_common.h"
 #include "attn_launch.h"
+#include "exp2_poly.h"
+
+// The FlashAttention-4 split of the softmax exponentials between the hardware
+// exponential and a polynomial on the FMA units (cheat sheet, FlashAttention-4
+// section), as a build option for measurement: with ATTN_EXP2_POLY_EVERY = n
+// > 0, one exponential in every n of a block goes to exp2_poly.  The default
+// build (0) keeps every exponential on v_exp_f32: on gfx950 both run on the
+// same VALU, and the polynomial's 8 instructions cost more issue cycles than
+// v_exp_f32 (bench.py --micro; the A/B with this option measured every split
+// slower).
+#ifndef ATTN_EXP2_POLY_EVERY
+#define ATTN_EXP2_POLY_EVERY 0
+#endif
 
 namespace attn_gfx950 {
 
@@ -427,7 +440,11 @@ __global__ __launch_bounds__((Tile<D, W>::kThreads)) __attribute__((amdgpu_waves
             float p[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -msub));
+                const float x = __builtin_fmaf(s[r], c_log2, -msub);
+                if (ATTN_EXP2_POLY_EVERY > 0 && r % (ATTN_EXP2_POLY_EVERY > 0 ? ATTN_EXP2_POLY_EVERY : 1) == ATTN_EXP2_POLY_EVERY - 1)
+                    p[r] = exp2_poly(x);
+                else
+                    p[r] = __builtin_amdgcn_exp2f(x);
                 if constexpr (MASKED)
                     p[r] = visible(k, r) ? p[r] : 0.f;
             }

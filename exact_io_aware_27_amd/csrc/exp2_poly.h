@@ -18,11 +18,15 @@
 // value (an exponent add: v_lshl_add_u32), which is exact while the result
 // stays a normal number.
 //
-// Domain: x is clamped below at -127, where the result is exactly +0
-// (j = -127, f = 0: the exponent add empties the exponent field); between
-// -127 and -126.5 the result is a tiny subnormal-pattern value below 2^-126.
-// Above, results are exact to the polynomial's error (plus fp32 rounding of
-// three FMAs) up to x = 127.  Cost: 8 VALU instructions (max, add, sub, sub,
+// Domain: for -125 <= x <= 127 the result is a normal number within
+// kExp2PolyRelErr of 2^x (the polynomial's error plus the fp32 rounding of
+// three FMAs).  Below, x is clamped at -126 so that the exponent add never
+// wraps (the polynomial's value at f = 0 is just under 1, so j = -127 would
+// carry into the sign and exponent bits and make a NaN): every x < -125,
+// -inf included, gives a non-negative value below 2^-124, possibly a
+// subnormal bit pattern that is not close to 2^x.  At that size a
+// probability is nothing next to a row whose largest term is at least 1;
+// masked keys are set to 0 separately.  Cost: 8 VALU instructions (max, add, sub, sub,
 // three FMAs, lshl_add) against one v_exp_f32.
 #pragma once
 
@@ -34,13 +38,13 @@ constexpr float kExp2C0 = 0.9999280571937561f;
 constexpr float kExp2C1 = 0.69326096773147583f;
 constexpr float kExp2C2 = 0.2426111251115799f;
 constexpr float kExp2C3 = 0.055171668529510498f;
-// Stated bound of exp2_poly's relative error over its domain (x >= -126):
+// Stated bound of exp2_poly's relative error for x >= -125:
 // the minimax error 7.5e-5 plus the fp32 rounding of the three FMAs.
 constexpr float kExp2PolyRelErr = 1e-4f;
 
 __device__ __forceinline__ float exp2_poly(float x)
 {
-    x = __builtin_fmaxf(x, -127.f);
+    x = __builtin_fmaxf(x, -126.f);
     const float t = x + 12582912.f;  // 1.5 * 2^23: round(x) in the low mantissa bits
     const float j = t - 12582912.f;
     const float f = x - j;  // exact, |f| <= 1/2
