@@ -515,6 +515,13 @@ def bench_micro(args):
                   % (k, e, m["exp"], w, m["cycles_per_mfma"], m["tflops"], m["clock_ghz"]),
                   file=sys.stderr, flush=True)
             mixes.append(m)
+    for k, e, shape in micro.SHAPED_MIXES:
+        for w in (1, 2):
+            m = micro.mix(k, e, False, w, shape=shape)
+            print("mix %d fma + %d exp per MFMA (%s), waves/SIMD %d: %.2f cycles/MFMA, %.0f TFLOP/s (%.2f GHz)"
+                  % (k, e, m["shape"], w, m["cycles_per_mfma"], m["tflops"], m["clock_ghz"]),
+                  file=sys.stderr, flush=True)
+            mixes.append(m)
     out = {"metric": "gfx950 issue rates (shader cycles), 1 GPU", "unit": "cycles", "rates": rates,
            "mixes": mixes, "note": "rate: per SIMD over all its waves (independent chains) or per dependent "
                                   "instruction; mix: per 32x32x16 bf16 MFMA per SIMD (32 = matrix-core rate)"}

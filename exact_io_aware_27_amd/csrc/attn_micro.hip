@@ -102,9 +102,12 @@ __global__ __launch_bounds__(1024) void rate_kernel(float *sink, unsigned long l
     sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s + (float)lds_pin[threadIdx.x & 7];
 }
 
-// Four MFMAs per iteration on independent accumulators; after each, K FMAs
-// and E exponentials (POLY: exp2_poly) on the 16 independent chains.
-template <int K, int E, bool POLY>
+// Four MFMAs per iteration on independent accumulators (CHAIN: all four on
+// one accumulator, each waiting for the last, as the score product's k-steps
+// do); after each, K FMAs and E exponentials (POLY: exp2_poly) on the 16
+// independent chains (PAIRED: each exponential takes the result of the FMA
+// just before it, as p = exp2(s c - m) does).
+template <int K, int E, bool POLY, bool CHAIN = false, bool PAIRED = false>
 __global__ __launch_bounds__(1024) void mix_kernel(float *sink, unsigned long long *times, int iters)
 {
     extern __shared__ char lds_pin[];
@@ -131,14 +134,30 @@ __global__ __launch_bounds__(1024) void mix_kernel(float *sink, unsigned long lo
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+            if constexpr (CHAIN)
+                acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[0], 0, 0, 0);
+            else
+                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+            if constexpr (PAIRED) {
+                // every chain takes one FMA per iteration; the last FMA of
+                // each group is followed at once by an exponential of its
+                // result, written back to the same chain
 #pragma unroll
-            for (int k = 0; k < K; ++k)
-                x[(j * (K + E) + k) % kChains] = apply<kOpFma>(x[(j * (K + E) + k) % kChains]);
+                for (int k = 0; k < K; ++k)
+                    x[(j * K + k) % kChains] = apply<kOpFma>(x[(j * K + k) % kChains]);
 #pragma unroll
-            for (int e = 0; e < E; ++e)
-                x[(j * (K + E) + K + e) % kChains] =
-                    apply<POLY ? kOpPoly : kOpExp>(x[(j * (K + E) + K + e) % kChains]);
+                for (int e = 0; e < E; ++e)
+                    x[(j * K + K - 1 - e) % kChains] =
+                        apply<POLY ? kOpPoly : kOpExp>(x[(j * K + K - 1 - e) % kChains]);
+            } else {
+#pragma unroll
+                for (int k = 0; k < K; ++k)
+                    x[(j * (K + E) + k) % kChains] = apply<kOpFma>(x[(j * (K + E) + k) % kChains]);
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    x[(j * (K + E) + K + e) % kChains] =
+                        apply<POLY ? kOpPoly : kOpExp>(x[(j * (K + E) + K + e) % kChains]);
+            }
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -266,19 +285,42 @@ extern "C" __attribute__((visibility("default"))) int attn_micro_rate(int op, in
     return 0;
 }
 
+extern "C" __attribute__((visibility("default"))) int attn_micro_mix_shape(int k_fma, int n_exp, int poly, int shape,
+                                                                           int waves_per_simd, int iters,
+                                                                           double *out);
+
 // One mix measurement: after each 32x32x16 bf16 MFMA, k_fma FMAs and n_exp
 // exponentials (poly: exp2_poly instead of v_exp_f32).  Instances:
 // (k, e) in (0,0) (2,1) (3,1) (4,1) (5,1) (6,1) (4,2) (8,0), and poly with
-// (3,1) (4,1).  out[0] = cycles per MFMA per SIMD (32 = the matrix core's
+// (3,1) (4,1); shape 1 runs (0,0) and (4,1) with the MFMAs on one dependent
+// accumulator chain, shape 2 runs (4,1) with each exponential taking the
+// FMA just before it.  out[0] = cycles per MFMA per SIMD (32 = the matrix core's
 // own rate for this shape), out[1] = shader clock (GHz), out[2] = ms,
 // out[3] = whole-chip bf16 TFLOP/s of the MFMAs.
 extern "C" __attribute__((visibility("default"))) int attn_micro_mix(int k_fma, int n_exp, int poly,
                                                                      int waves_per_simd, int iters, double *out)
 {
+    return attn_micro_mix_shape(k_fma, n_exp, poly, 0, waves_per_simd, iters, out);
+}
+
+// attn_micro_mix with a dependence shape: 0 as attn_micro_mix, 1 the MFMAs
+// on one accumulator chain, 2 each exponential taking the FMA before it.
+extern "C" __attribute__((visibility("default"))) int attn_micro_mix_shape(int k_fma, int n_exp, int poly, int shape,
+                                                                           int waves_per_simd, int iters,
+                                                                           double *out)
+{
     double cyc = 0, ghz = 0, ms = 0;
     int st = 2;
+    if (shape == 1 && !poly && ((k_fma == 0 && n_exp == 0) || (k_fma == 4 && n_exp == 1))) {
+        st = k_fma ? run(mix_kernel<4, 1, false, true, false>, waves_per_simd, iters, &cyc, &ghz, &ms)
+                   : run(mix_kernel<0, 0, false, true, false>, waves_per_simd, iters, &cyc, &ghz, &ms);
+    } else if (shape == 2 && !poly && k_fma == 4 && n_exp == 1) {
+        st = run(mix_kernel<4, 1, false, false, true>, waves_per_simd, iters, &cyc, &ghz, &ms);
+    } else if (shape != 0) {
+        return 2;
+    }
 #define ATTN_MICRO_MIX(K, E, P)                                                                 \
-    if (k_fma == K && n_exp == E && (poly != 0) == P)                                           \
+    if (shape == 0 && k_fma == K && n_exp == E && (poly != 0) == P)                             \
         st = run(mix_kernel<K, E, P>, waves_per_simd, iters, &cyc, &ghz, &ms);
     ATTN_MICRO_MIX(0, 0, false)
     ATTN_MICRO_MIX(2, 1, false)

@@ -31,6 +31,8 @@ def load():
     lib.attn_micro_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, d4]
     lib.attn_micro_mix.restype = ctypes.c_int
     lib.attn_micro_mix.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, d4]
+    lib.attn_micro_mix_shape.restype = ctypes.c_int
+    lib.attn_micro_mix_shape.argtypes = [ctypes.c_int] * 6 + [d4]
     lib.attn_micro_exp2.restype = ctypes.c_int
     lib.attn_micro_exp2.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
                                     ctypes.c_void_p]
@@ -51,14 +53,19 @@ def rate(op, waves_per_simd, dependent=False, iters=20000):
             "clock_ghz": out[1], "ms": out[2]}
 
 
-def mix(k_fma, n_exp, poly, waves_per_simd, iters=20000):
+SHAPES = {0: "independent", 1: "one MFMA accumulator chain", 2: "each exp on the FMA before it"}
+SHAPED_MIXES = [(0, 0, 1), (4, 1, 1), (4, 1, 2)]
+
+
+def mix(k_fma, n_exp, poly, waves_per_simd, iters=20000, shape=0):
     """Cycles per 32x32x16 bf16 MFMA per SIMD with k_fma FMAs and n_exp
-    exponentials after each MFMA (32 = the matrix core's own rate)."""
+    exponentials after each MFMA (32 = the matrix core's own rate); shape
+    as SHAPES."""
     out = (ctypes.c_double * 4)()
-    st = load().attn_micro_mix(k_fma, n_exp, 1 if poly else 0, waves_per_simd, iters, out)
+    st = load().attn_micro_mix_shape(k_fma, n_exp, 1 if poly else 0, shape, waves_per_simd, iters, out)
     if st:
         raise RuntimeError("attn_micro_mix status %d" % st)
-    return {"k_fma": k_fma, "n_exp": n_exp, "exp": "exp2_poly" if poly else "v_exp_f32",
+    return {"k_fma": k_fma, "n_exp": n_exp, "exp": "exp2_poly" if poly else "v_exp_f32", "shape": SHAPES[shape],
             "waves_per_simd": waves_per_simd, "cycles_per_mfma": out[0], "clock_ghz": out[1],
             "ms": out[2], "tflops": out[3]}
 
