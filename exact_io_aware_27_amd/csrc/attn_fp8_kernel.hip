@@ -18,8 +18,8 @@
 //   * Incoherent processing: x -> (x * s) H, random signs s, then the
 //     Sylvester Hadamard matrix H by its fast transform in fp32 (butterfly
 //     stages of stride 1, 2, ..., 64, each (a, b) -> (a + b, a - b)).  The
-//     product of rotated Q and K is d times the original: the caller divides
-//     the softmax scale by d.
+//     product of rotated Q and K is d times the original: attn_fwd_fp8
+//     divides d out of the softmax scale when told the inputs are rotated.
 //   * Q and K: [BH][Np][128] bytes, Np = N rounded up to 64, rows past N zero.
 //     V: transposed, [BH][128][Np], and within every 64-key tile the keys are
 //     stored in the order the P operand of the P V product holds them: key r
