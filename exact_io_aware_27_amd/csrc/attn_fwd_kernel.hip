@@ -13,9 +13,10 @@
 //
 // gfx950 mapping
 //   * 32 query rows per 64-lane wave.  d = 128: 8 waves (256 queries) per
-//     workgroup, one workgroup per CU; d = 64, and key ranges of a few query
-//     rows (decoding) at d = 128: 4 waves (128 queries), two workgroups per
-//     CU.  Either way two waves share each SIMD.
+//     workgroup, one workgroup per CU; key ranges of a few query rows
+//     (decoding) at d = 128: 4 waves (128 queries), two workgroups per CU;
+//     either way two waves share each SIMD.  d = 64: 4 waves, three
+//     workgroups per CU (three waves per SIMD).
 //   * Each wave computes the TRANSPOSED score tile S^T = K Q^T with
 //     v_mfma_f32_32x32x16_bf16: in the 32x32 accumulator layout a lane holds
 //     one column (one query) and 16 of the 32 rows (keys), so a query's row
@@ -184,13 +185,24 @@ struct KArgs {
     float c_log2;
 };
 
-// Two waves per SIMD is the design point (one 8-wave workgroup per CU for
-// d = 128, two 4-wave ones for d = 64), so the register budget is stated as
-// exactly that: without it the scheduler keeps a step in source order
-// whenever the interleaved MFMA/softmax order would cross the three-wave
-// register threshold (168 VGPRs), which costs up to 8%.
+// Waves per SIMD, stated as the register budget.  d = 128: two (one 8-wave
+// workgroup per CU, 256 VGPRs each); without the statement the scheduler
+// keeps a step in source order whenever the interleaved MFMA/softmax order
+// would cross the three-wave register threshold (168 VGPRs), which costs up
+// to 8%.  d = 64: three (three 4-wave workgroups per CU, 168 VGPRs, no VGPR
+// spill): the short d = 64 launches spend much of a workgroup's life in its
+// prologue, and a third resident workgroup hides more of it (same-box A/B,
+// bitwise-equal output: +3-5% on every d = 64 shape measured, B=8 H=12
+// N=1024 causal 457 -> 475 TFLOP/s).
+template <int D>
+constexpr int waves_per_simd()
+{
+    return D == 64 ? 3 : 2;
+}
+
 template <int D, bool CAUSAL, bool SPLIT, int W>
-__global__ __launch_bounds__((Tile<D, W>::kThreads)) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(
+__global__ __launch_bounds__((Tile<D, W>::kThreads)) __attribute__((
+    amdgpu_waves_per_eu(waves_per_simd<D>(), waves_per_simd<D>()))) void attn_fwd_kernel(
     const KArgs a)
 {
     // The body is device code only (gfx950 buffer resources and LDS builtins);
@@ -876,10 +888,11 @@ static hipError_t launch(const AttnLaunch &a, int splits, int split_keys)
     k.split_keys = split_keys;
     // Causal, one key range: pairs of query tiles, or single tiles longest
     // first when the pairs would not fill the chip's workgroup slots twice
-    // (256 CUs, 8 / W workgroups each) and the heads split evenly over the
-    // XCDs.
+    // (256 CUs, 4 SIMDs x waves_per_simd / W workgroups each) and the heads
+    // split evenly over the XCDs.
     const int64_t pairs = a.BH * ((k.nqt + 1) / 2);
-    k.lpt = CAUSAL && !SPLIT && a.BH % kXcds == 0 && pairs < 2 * 256 * (8 / W);
+    const int64_t slots = 256 * (4 * waves_per_simd<D>() / W);
+    k.lpt = CAUSAL && !SPLIT && a.BH % kXcds == 0 && pairs < 2 * slots;
     k.n_wg = (int)(a.BH * ((CAUSAL && !k.lpt) ? (k.nqt + 1) / 2 : k.nqt) * splits);
     k.c_log2 = a.scale * kLog2e;
     hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, SPLIT, W>), dim3(k.n_wg), dim3(T::kThreads), 0, a.stream, k);
