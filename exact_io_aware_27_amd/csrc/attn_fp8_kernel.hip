@@ -410,6 +410,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         bool pending = false;
         float alpha_pend = 1.f;
         i32x8 pb_prev = i32x8{};
+        // Block exponents, loaded one step ahead of their use, so that no
+        // scalar load's latency sits in front of a step's first MFMA (the
+        // steps' rare branches keep the compiler from hoisting them): ks_next
+        // is that of the K block whose scores the next step forms, vs_next
+        // that of the V block whose P V it accumulates.
+        int ks_next = exp_of(a.ke, 1), vs_next = kE8M0One;
 
         // One 64-key step: block s = 2 t + J of tile t (K buffer P = t % 2).
         // The softmax of block s interleaves with the scores of block s+1 and
@@ -438,7 +444,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 load_k(t + 2, kown);
                 load_v(t + 1, vother);
             }
-            const int ks = exp_of(a.ke, blk + 1), vs = blk > 0 ? exp_of(a.ve, blk - 1) : kE8M0One;
+            const int ks = ks_next, vs = vs_next;
+            ks_next = exp_of(a.ke, blk + 2);
+            vs_next = exp_of(a.ve, blk);
             // Keep the LDS offsets opaque (so they ride in the ds_read offset
             // field instead of being hoisted as per-buffer sums) and the
             // softmax inside its step.
@@ -510,13 +518,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             }
             asm volatile("" : "+v"(pb), "+v"(l_run));
 
-            if (pending) {
+            // Both branches are rare: laid out off the step's straight line,
+            // so that a step runs into the next without a taken branch.
+            if (__builtin_expect(pending, 0)) {
 #pragma unroll
                 for (int b = 0; b < 4; ++b)
                     oacc[b] *= alpha_pend;
             }
             pending = reref;
-            if (reref) {
+            if (__builtin_expect(reref, 0)) {
                 const float m_new = fmaxf(m_ref, wave_half_max(mx));
                 alpha_pend = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
                 l_run *= alpha_pend;
@@ -571,16 +581,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         // in flight before the next pass reuses the buffers.
         {
             char *vlast = ((t_end - 1) & 1) ? sv1 : sv0;
-            const int vs = exp_of(a.ve, 2 * t_end - 1);
+            const int vs = vs_next;
 #pragma unroll
             for (int db = 0; db < 4; ++db)
                 oacc[db] = mfma8(lds_pair(vlast + db * 32 * kD + voff[1][0], vlast + db * 32 * kD + voff[1][1]),
                                  pb_prev, oacc[db], vs, kE8M0One);
-            if (pending) {
+            if (__builtin_expect(pending, 0)) {
 #pragma unroll
                 for (int b = 0; b < 4; ++b)
                     oacc[b] *= alpha_pend;
             }
+            // O is read only by the lanes of valid queries: keep these MFMAs
+            // out of that lane-masked branch (an MFMA under a partial EXEC mask
+            // does not compute the lanes' tile).
+            asm volatile("" : "+v"(oacc[0]), "+v"(oacc[1]), "+v"(oacc[2]), "+v"(oacc[3]));
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();

@@ -593,8 +593,9 @@ __global__ __launch_bounds__((Tile<D, W>::kThreads)) __attribute__((
                 // the reference: move the reference to the row's exact running max
                 // (this block's scores are still in registers), rescale l, lb and
                 // O (which now holds P V up to block k-1, all against the old
-                // reference), and take this block's probabilities again.
-                if (reref) {
+                // reference), and take this block's probabilities again.  (Rare:
+                // laid out off the step's straight line.)
+                if (__builtin_expect(reref, 0)) {
                     float mb = kNegInf;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
@@ -616,8 +617,9 @@ __global__ __launch_bounds__((Tile<D, W>::kThreads)) __attribute__((
             } else {
                 // The reference moved at the previous step: O now holds P V of
                 // block k-1 as well, taken against the old reference, so rescale
-                // it here.
-                if (pending) {
+                // it here.  (Both branches are rare: laid out off the step's
+                // straight line.)
+                if (__builtin_expect(pending, 0)) {
 #pragma unroll
                     for (int b = 0; b < T::kOBlocks; ++b)
                         oacc[b] *= alpha_pend;
@@ -627,7 +629,7 @@ __global__ __launch_bounds__((Tile<D, W>::kThreads)) __attribute__((
                 // max (both halves of the row) and rescale the sums now, O after
                 // the next P V.
                 pending = reref;
-                if (reref) {
+                if (__builtin_expect(reref, 0)) {
                     const float m_new = fmaxf(m_ref, wave_half_max(mx));
                     alpha_pend = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
                     l_run *= alpha_pend;
@@ -778,12 +780,18 @@ __global__ __launch_bounds__((Tile<D, W>::kThreads)) __attribute__((
             }
             // P V of the last block: second half of V tile t_end-1.
             pv((t_end - 1) & 1 ? sv1 : sv0, 32 * T::kRowBytes, pb_prev);
-            if (pending) {
+            if (__builtin_expect(pending, 0)) {
 #pragma unroll
                 for (int b = 0; b < T::kOBlocks; ++b)
                     oacc[b] *= alpha_pend;
             }
         }
+        // O is read only by the lanes of valid queries: keep its MFMAs out of
+        // that lane-masked branch (an MFMA under a partial EXEC mask does not
+        // compute the lanes' tile).
+#pragma unroll
+        for (int b = 0; b < T::kOBlocks; ++b)
+            asm volatile("" : "+v"(oacc[b]));
         __builtin_amdgcn_s_waitcnt(0);  // no copy may still be writing LDS when the workgroup ends
 
         // Epilogue: O = O / lb (the sum of the bf16 weights that built O),

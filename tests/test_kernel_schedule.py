@@ -141,3 +141,34 @@ def test_no_scratch_in_backward_and_fp8_key_loops(other_asm, key):
         key_loops, spills = key_loop_spills(_instance(lines, name))
         assert key_loops, "%s: no key loop found" % name
         assert not spills, "%s: scratch access inside a key loop: %s" % (name, spills[:3])
+
+
+def mfma_inside_output_branch(body):
+    """MFMAs between the last lane-masking s_and_saveexec before the first
+    store of the output and that store: the body of the branch that only
+    the lanes of valid queries run."""
+    store = next(i for i, l in enumerate(body) if l.strip().startswith(("global_store", "buffer_store")))
+    masks = [i for i in range(store) if body[i].strip().startswith(("s_and_saveexec", "s_and_b64 exec, exec"))]
+    if not masks:
+        return []
+    return [body[i].strip() for i in range(masks[-1], store) if body[i].strip().startswith("v_mfma")]
+
+
+@pytest.mark.parametrize("instance", INSTANCES)
+def test_output_mfmas_run_with_every_lane(asm, instance):
+    """The last P V MFMAs feed only the stores of valid query rows; the
+    compiler may sink them into that lane-masked branch, where an MFMA does
+    not compute the rows of the live lanes (seen as wrong rows in a tile
+    whose last wave holds a few valid queries).  The kernel pins O after
+    them; this checks the compiled result."""
+    bad = mfma_inside_output_branch(_instance(asm, instance))
+    assert not bad, "MFMA inside the output branch: %s" % bad[:2]
+
+
+def test_fp8_output_mfmas_run_with_every_lane(other_asm):
+    lines = other_asm["fp8"]
+    names = [l.split(":")[0] for l in lines if re.match(r"^_ZN\w+:", l) and "quantize" not in l]
+    assert len(names) == 2, names
+    for name in names:
+        bad = mfma_inside_output_branch(_instance(lines, name))
+        assert not bad, "%s: MFMA inside the output branch: %s" % (name, bad[:2])
