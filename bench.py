@@ -42,14 +42,18 @@ def code_only(text):
 
 
 def compiler_id():
-    """hipcc's version text: a compiler change changes the generated code."""
+    """hipcc's version lines (HIP and clang): a compiler change changes the
+    generated code.  Only those lines, so that the id is the same on every
+    machine with the same compiler (hipcc may add warnings about the host's
+    devices on stderr)."""
     import subprocess
 
     from exact_io_aware_27_amd import build
     try:
-        return subprocess.check_output([build.HIPCC, "--version"], text=True, stderr=subprocess.STDOUT)
+        text = subprocess.check_output([build.HIPCC, "--version"], text=True, stderr=subprocess.DEVNULL)
     except (OSError, subprocess.CalledProcessError):
         return "hipcc unavailable"
+    return "\n".join(l for l in text.splitlines() if l.startswith(("HIP version", "AMD clang version")))
 
 
 def kernel_hash():
