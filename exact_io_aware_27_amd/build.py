@@ -7,7 +7,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libattn.so")
-SOURCES = ["attn_api.hip", "attn_fwd_kernel.hip", "attn_bwd_kernel.hip", "attn_fp8_kernel.hip"]
+SOURCES = ["attn_api.hip", "attn_fwd_kernel.hip", "attn_decode_kernel.hip", "attn_bwd_kernel.hip", "attn_fp8_kernel.hip"]
 # the issue-rate microbenchmarks (bench.py --micro) and the exp2_poly accuracy
 # kernel: a separate library, not part of the attention ABI
 MICRO_LIB = os.path.join(PKG, "libattn_micro.so")

@@ -876,6 +876,19 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float *__restrict
         LSE[row] = wsum > 0.f ? m + __builtin_logf(wsum) : kNegInf;
 }
 
+// The merge of the key ranges in the split workspace into O and LSE.
+template <int D>
+static hipError_t merge_launch(const AttnLaunch &a, int splits)
+{
+    const float *opart = (const float *)a.workspace;
+    const float *lsepart = opart + (size_t)splits * a.BH * a.Nq * D;
+    const int rows = (int)(a.BH * a.Nq);
+    const int threads = rows * (D / 8);
+    hipLaunchKernelGGL((attn_merge_kernel<D>), dim3((threads + 255) / 256), dim3(256), 0, a.stream, opart, lsepart,
+                       (__bf16 *)a.o, a.lse, rows, splits);
+    return hipGetLastError();
+}
+
 template <int D, bool CAUSAL, bool SPLIT, int W = Tile<D>::kWaves>
 static hipError_t launch(const AttnLaunch &a, int splits, int split_keys)
 {
@@ -907,11 +920,7 @@ static hipError_t launch(const AttnLaunch &a, int splits, int split_keys)
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || !SPLIT)
         return err;
-    const int rows = (int)(a.BH * a.Nq);
-    const int threads = rows * (D / 8);
-    hipLaunchKernelGGL((attn_merge_kernel<D>), dim3((threads + 255) / 256), dim3(256), 0, a.stream,
-                       (const float *)k.Opart, (const float *)k.LSEpart, (__bf16 *)a.o, a.lse, rows, splits);
-    return hipGetLastError();
+    return merge_launch<D>(a, splits);
 }
 
 template <int D, bool CAUSAL>
@@ -920,6 +929,12 @@ static hipError_t launch_mode(const AttnLaunch &a)
     const int64_t splits = attn_splits_used(a.Nk, a.num_splits);
     if (splits <= 1)
         return launch<D, CAUSAL, false>(a, 1, (int)attn_split_keys(a.Nk, 1));
+    if (a.Nq <= kDecodeRows) {  // a few query rows: the streaming kernel, then the merge
+        const hipError_t err = attn_decode_ranges_launch(a, (int)splits, (int)attn_split_keys(a.Nk, a.num_splits));
+        if (err != hipSuccess)
+            return err;
+        return merge_launch<D>(a, (int)splits);
+    }
     if constexpr (D == 128) {
         if (a.Nq <= 128)  // decoding: one 4-wave query tile per head and range
             return launch<D, CAUSAL, true, 4>(a, (int)splits, (int)attn_split_keys(a.Nk, a.num_splits));

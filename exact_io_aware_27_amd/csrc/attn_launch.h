@@ -35,6 +35,12 @@ int64_t attn_workgroups(int64_t BH, int64_t Nq, int64_t Nk, int64_t num_splits);
 // Enqueue the kernel(s); returns hipGetLastError() after the launches.
 hipError_t attn_launch(const AttnLaunch &a);
 
+// Key ranges of a call with at most kDecodeRows query rows per head:
+// writes every range's normalised fp32 O and LSE into the split workspace
+// (the layout of the forward kernel's split mode), for the merge kernel.
+constexpr int64_t kDecodeRows = 4;
+hipError_t attn_decode_ranges_launch(const AttnLaunch &a, int splits, int split_keys);
+
 // Arguments of one validated backward call (attn_bwd).  d is 64 or 128,
 // N * d is below 2^31 and the workgroup count fits in an int.
 struct AttnBwdLaunch {

@@ -68,7 +68,7 @@ def test_prefill_splits_match_oracle(N, S, d, causal):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("Nq", [1000, 33])
+@pytest.mark.parametrize("Nq", [1000, 33, 3])
 def test_growing_scores_move_the_reference_in_every_range(Nq, d, causal):
     """Large logits (Q, K ~ N(0, 4^2)) on keys whose norm grows along the
     sequence, cut into 3 ranges: the reference moves many times inside each
@@ -86,8 +86,13 @@ def test_growing_scores_move_the_reference_in_every_range(Nq, d, causal):
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("Nq,Nk,S", [
     (1, 1, 1), (1, 1, 4), (1, 127, 4), (1, 128, 4), (1, 129, 4), (1, 1000, 1), (1, 1000, 4),
-    (1, 4097, 16), (4, 1000, 8), (33, 1000, 3), (33, 4097, 16), (257, 4097, 5)])
+    (1, 4097, 16), (2, 1000, 4), (3, 4097, 16), (4, 1000, 8), (4, 130, 2), (5, 1000, 4),
+    (33, 1000, 3), (33, 4097, 16), (257, 4097, 5)])
 def test_decode_shapes_match_oracle(Nq, Nk, S, d, causal):
+    """Up to four query rows per head take the streaming key-range kernel,
+    more take the forward kernel's split mode.  Nk = 130, Nq = 4, causal:
+    the first query sees no key of the second range (its LSE there is
+    -inf); ragged key counts leave partial 4- and 8-key slots."""
     q, k, v = qkv(2, 2, Nq, Nk, d, seed=4000 + Nq + Nk + S + d + causal)
     check(q, k, v, causal, S, "Nq=%d Nk=%d d=%d" % (Nq, Nk, d))
 
