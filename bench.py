@@ -64,7 +64,17 @@ def kernel_hash():
     for p in KERNEL_SOURCES:
         with open(p) as f:
             h.update(code_only(f.read()).encode())
-    h.update(" ".join(build.FLAGS).encode())
+    # the flags, less the include directory's location (a checkout's path,
+    # which differs between machines and does not change the code)
+    flags, skip = [], False
+    for f in build.FLAGS:
+        if skip:
+            skip = False
+        elif f == "-I":
+            skip = True
+        else:
+            flags.append(f)
+    h.update(" ".join(flags).encode())
     h.update(compiler_id().encode())
     return h.hexdigest()[:16]
 
