@@ -478,8 +478,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
             for (int w = 0; w < 8; ++w) {
                 const float *pp = &p[w >> 2][4 * (w & 3)];
-                int u = __builtin_amdgcn_cvt_pk_fp8_f32(pp[0], pp[1], 0, false);
-                pb[w] = __builtin_amdgcn_cvt_pk_fp8_f32(pp[2], pp[3], u, true);
+                // Low half, then high half into the same register.  As asm, the
+                // first conversion needs no register cleared before it (the
+                // builtin's "old" operand is a zero the compiler materialises
+                // with a v_mov, 8 per step, though the high half is written
+                // next).
+                int u;
+                asm("v_cvt_pk_fp8_f32 %0, %1, %2" : "=v"(u) : "v"(pp[0]), "v"(pp[1]));
+                asm("v_cvt_pk_fp8_f32 %0, %1, %2 op_sel:[0,0,1]" : "+v"(u) : "v"(pp[2]), "v"(pp[3]));
+                pb[w] = u;
             }
 
             f32x16 sn[2];
