@@ -181,7 +181,7 @@ def bench_parity(args):
     workloads; the seeded row subsets of the large-logit and very long ones,
     rows 0 and N-1 included), with the literal max/mean |dO| and max |dLSE|
     next to the oracle-only bf16 rounding floor (|bf16(O_ref) - O_ref|) and
-    the verdict under both the literal max bar and the 1e-2 + half-ulp one."""
+    the outcome under both the literal max bar and the 1e-2 + half-ulp one."""
     import numpy as np
     import torch
 
@@ -561,7 +561,7 @@ def main():
                     help="parity report against the fp64 oracle: 'all' or comma-separated workload names; "
                          "one JSON line per workload (exit 3 if one fails its bar)")
     ap.add_argument("--lib", default=None,
-                    help="load this build of the attention library instead of the in-tree one (A/B of build "
+                    help="load this libattn.so instead of the in-tree one (A/B of build "
                          "options, see exact_io_aware_27_amd/build.py --out)")
     ap.add_argument("--micro", action="store_true",
                     help="gfx950 issue-rate microbenchmarks (VALU, exp, exp2_poly, MFMA mixes) in shader cycles")
@@ -584,7 +584,7 @@ def main():
         attn.LIB_PATH = os.path.abspath(args.lib)
 
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
+        print("bench.py: the attention library runs on one GPU only; --gpus %d is not supported "
               "(the path has no multi-GPU mode)" % args.gpus, file=sys.stderr)
         return 2
 
