@@ -56,6 +56,32 @@ def compiler_id():
     return "\n".join(l for l in text.splitlines() if l.startswith(("HIP version", "AMD clang version")))
 
 
+def device_clock_ghz():
+    """The peak shader clock the HIP runtime reports for device 0, in GHz
+    (hipDeviceAttributeClockRate, in kHz), or None.  The dense bf16 peak
+    derived from it and the CU count (4096 flops per CU per clock: four
+    matrix cores, each a 32x32x16 MFMA of 32768 flops every 32 clocks) is
+    printed beside the published one."""
+    import ctypes
+    try:
+        hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch and libattn.so already hold
+    except OSError:
+        return None
+    khz = ctypes.c_int(0)
+    attr_clock_rate = 5  # hipDeviceAttributeClockRate, sixth entry of hipDeviceAttribute_t
+    if hip.hipDeviceGetAttribute(ctypes.byref(khz), attr_clock_rate, 0) != 0 or khz.value <= 0:
+        return None
+    return khz.value / 1e6
+
+
+def device_info(props):
+    ghz = device_clock_ghz()
+    return {"name": props.name, "cus": props.multi_processor_count,
+            "gcn_arch": getattr(props, "gcnArchName", None), "clock_ghz": ghz,
+            "bf16_peak_from_device_tflops": (round(props.multi_processor_count * 4096 * ghz / 1e3, 1)
+                                             if ghz else None)}
+
+
 def kernel_hash():
     """Hash of what the forward kernel's machine code depends on: its source
     (comments excluded), the build flags and the compiler version."""
@@ -163,6 +189,8 @@ def cpu_baseline(w, q, k, v, o_gpu, lse_gpu, rows_per_head):
         "sample": "%d seeded query rows per head (%d of %d rows, rows 0 and N-1 included), "
                   "every visible key of each row; %.3g counted flops in %.1f s"
                   % (rows_per_head, rows.numel(), w.B * w.H * w.N, flops, dt),
+        # the whole workload at the sample's rate (rows weighted by their visible keys)
+        "extrapolated_all_rows_s": round(w.flops / (flops / dt), 1),
     }, {"rows": int(rows.numel()), "max_abs_dO": float(do.max()), "mean_abs_dO": float(do.mean()),
         "max_abs_dLSE": float(dl.max()), "n_over_relaxed": int((do > 1e-2 + half_ulp).sum())}
 
@@ -695,8 +723,7 @@ def main():
                 "measured_bytes": traffic,
                 "measured_GBps": (round(traffic / (ms * 1e-3) / 1e9, 1) if traffic else None),
                 "peak_GBps": HBM_PEAK_GBPS},
-        "device": {"name": props.name, "cus": props.multi_processor_count,
-                   "gcn_arch": getattr(props, "gcnArchName", None)},
+        "device": device_info(props),
         "kernel_hash": kernel_hash() if not args.lib else None,
         "library": os.path.relpath(attn.LIB_PATH, ROOT),
         "context_other_hardware": {
