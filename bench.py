@@ -456,16 +456,16 @@ def bench_fp8(args):
     signs = inputs.make_signs(w.d, seed=w.seed + 1).numpy()
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     stream = torch.cuda.current_stream(dev)
-    q8, qe = attn.fp8_quantize(qd, signs=signs, stream=stream)
+    q8, qe = attn.fp8_quantize(qd, signs=signs, stream=stream, scale=w.scale)
     k8, ke = attn.fp8_quantize(kd, signs=signs, stream=stream)
     vt8, ve = attn.fp8_quantize(vd, transpose=True, stream=stream)
     od = torch.empty_like(qd)
     lsed = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     def attend():
-        attn.attn_fwd_fp8(q8, k8, vt8, qe, ke, ve, od, lsed, w.B, w.H, w.N, w.d, w.causal, w.scale, True, stream)
+        attn.attn_fwd_fp8(q8, k8, vt8, qe, ke, ve, od, lsed, w.B, w.H, w.N, w.d, w.causal, stream)
 
     def quantize():
-        attn.fp8_quantize_status(qd, w.B, w.H, w.N, w.d, False, signs, q8, qe, stream)
+        attn.fp8_quantize_status(qd, w.B, w.H, w.N, w.d, False, signs, q8, qe, stream, w.scale)
         attn.fp8_quantize_status(kd, w.B, w.H, w.N, w.d, False, signs, k8, ke, stream)
         attn.fp8_quantize_status(vd, w.B, w.H, w.N, w.d, True, None, vt8, ve, stream)
 
@@ -500,12 +500,12 @@ def bench_fp8(args):
         R = min(args.cpu_rows, w.N)
         rows = inputs.row_subset(w.N, R, w.seed, 0, (0, w.N - 1)).numpy()
         t0 = time.perf_counter()
-        prep = f8.prepare_fp8(q[:1, :1], k[:1, :1], v[:1, :1], signs=signs)
+        prep = f8.prepare_fp8(q[:1, :1], k[:1, :1], v[:1, :1], signs=signs, scale=w.scale)
         o_ref, lse_ref, sig = [], [], []
         for r in rows:
             hi = r + 1 if w.causal else w.N
             a, b_, c = f8.attention_fp64(prep["q"][:, :, [r]], prep["k"][:, :, :hi], prep["v"][:, :, :hi], False,
-                                         w.scale / prep["qk_factor"], p_rounding=True)
+                                         prep["qk_mul"], p_rounding=True)
             o_ref.append(a), lse_ref.append(b_), sig.append(c)
         dt = time.perf_counter() - t0
         o_ref, lse_ref, sig = (np.concatenate(x, axis=2) for x in (o_ref, lse_ref, sig))

@@ -26,7 +26,7 @@ STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_NULL_PTR", 2: "ATTN_BAD_SHAPE", 3: "ATTN_
                 8: "ATTN_BAD_WORKSPACE", 9: "ATTN_BAD_ARGUMENT", 10: "ATTN_SCRATCH_TOO_SMALL"}
 EXPORTS = ("attn_fwd", "attn_fwd_splitkv", "attn_fwd_splitkv_noalloc", "attn_noalloc_scratch_bytes",
            "attn_fwd_splitkv_workspace_bytes", "attn_bwd",
-           "attn_bwd_workspace_bytes", "attn_fp8_padded_rows", "attn_fp8_quantize", "attn_fwd_fp8",
+           "attn_bwd_workspace_bytes", "attn_fp8_padded_rows", "attn_fp8_quantize", "attn_fp8_quantize_q", "attn_fwd_fp8",
            "attn_status_string", "attn_last_hip_error")
 
 _lib = None
@@ -75,8 +75,10 @@ def load():
     lib.attn_fp8_quantize.restype = ctypes.c_int
     lib.attn_fp8_quantize.argtypes = [p, i64, i64, i64, i64, ctypes.c_int, p, p, p, p]
     lib.attn_fwd_fp8.restype = ctypes.c_int
-    lib.attn_fwd_fp8.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, ctypes.c_int, ctypes.c_float,
-                                 ctypes.c_int, p]
+    lib.attn_fp8_quantize_q.restype = ctypes.c_int
+    lib.attn_fp8_quantize_q.argtypes = [p, i64, i64, i64, i64, p, ctypes.c_float, p, p, p]
+    lib.attn_fwd_fp8.restype = ctypes.c_int
+    lib.attn_fwd_fp8.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, ctypes.c_int, p]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_status_string.argtypes = [ctypes.c_int]
     lib.attn_last_hip_error.restype = ctypes.c_int
@@ -310,17 +312,25 @@ def sign_bits(signs):
     return words
 
 
-def fp8_quantize_status(x, B, H, N, d, transpose, signs, out, exps, stream=None):
-    """Call attn_fp8_quantize and return its status.  signs: None or +-1 [128]."""
+def fp8_quantize_status(x, B, H, N, d, transpose, signs, out, exps, stream=None, scale=None):
+    """Call attn_fp8_quantize (scale None: K or V) or attn_fp8_quantize_q
+    (scale given: Q, with transpose False) and return its status.  signs:
+    None or +-1 [128]."""
     lib = load()
     bits = None if signs is None else sign_bits(signs)
-    return lib.attn_fp8_quantize(_ptr(x), int(B), int(H), int(N), int(d), 1 if transpose else 0,
-                                 None if bits is None else ctypes.cast(bits, ctypes.c_void_p),
+    bits_p = None if bits is None else ctypes.cast(bits, ctypes.c_void_p)
+    if scale is not None:
+        if transpose:
+            raise ValueError("Q is quantized without the transposed layout")
+        return lib.attn_fp8_quantize_q(_ptr(x), int(B), int(H), int(N), int(d), bits_p, float(scale),
+                                       _ptr(out), _ptr(exps), _stream(stream))
+    return lib.attn_fp8_quantize(_ptr(x), int(B), int(H), int(N), int(d), 1 if transpose else 0, bits_p,
                                  _ptr(out), _ptr(exps), _stream(stream))
 
 
-def fp8_quantize(x, transpose=False, signs=None, stream=None):
-    """Quantize a contiguous bf16 CUDA tensor [B, H, N, 128] to FP8.
+def fp8_quantize(x, transpose=False, signs=None, stream=None, scale=None):
+    """Quantize a contiguous bf16 CUDA tensor [B, H, N, 128] to FP8 (with
+    `scale`, the softmax scale: as Q, by attn_fp8_quantize_q).
 
     Returns (codes, exps): uint8 tensors [B, H, Np, 128] (or [B, H, 128, Np]
     with transpose, in the kernel's key order) and [B, H, Np // 64].
@@ -333,25 +343,24 @@ def fp8_quantize(x, transpose=False, signs=None, stream=None):
     exps = torch.empty((B, H, Np // 64), dtype=torch.uint8, device=x.device)
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
-    st = fp8_quantize_status(x, B, H, N, d, transpose, signs, out, exps, stream)
+    st = fp8_quantize_status(x, B, H, N, d, transpose, signs, out, exps, stream, scale)
     if st != ATTN_OK:
         raise AttnError(st, load().attn_last_hip_error() if st == 7 else 0)
     return out, exps
 
 
-def attn_fwd_fp8_status(q8, k8, vt8, qe, ke, ve, o, lse, B, H, N, d, causal, scale, rotated, stream=None):
+def attn_fwd_fp8_status(q8, k8, vt8, qe, ke, ve, o, lse, B, H, N, d, causal, stream=None):
     """Call attn_fwd_fp8 and return its status (0 = ATTN_OK)."""
     _check(o, "o", (int(B), int(H), int(N), int(d)), torch.bfloat16)
     _check(lse, "lse", (int(B), int(H), int(N)), torch.float32)
     lib = load()
     return lib.attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(vt8), _ptr(qe), _ptr(ke), _ptr(ve), _ptr(o), _ptr(lse),
-                            int(B), int(H), int(N), int(d), 1 if causal else 0, float(scale),
-                            1 if rotated else 0, _stream(stream))
+                            int(B), int(H), int(N), int(d), 1 if causal else 0, _stream(stream))
 
 
-def attn_fwd_fp8(q8, k8, vt8, qe, ke, ve, o, lse, B, H, N, d, causal, scale, rotated, stream=None):
+def attn_fwd_fp8(q8, k8, vt8, qe, ke, ve, o, lse, B, H, N, d, causal, stream=None):
     """attn_fwd_fp8 of include/attn.h; raises AttnError on a nonzero status."""
-    st = attn_fwd_fp8_status(q8, k8, vt8, qe, ke, ve, o, lse, B, H, N, d, causal, scale, rotated, stream)
+    st = attn_fwd_fp8_status(q8, k8, vt8, qe, ke, ve, o, lse, B, H, N, d, causal, stream)
     if st != ATTN_OK:
         raise AttnError(st, load().attn_last_hip_error() if st == 7 else 0)
 
@@ -365,10 +374,10 @@ def attention_fp8(q, k, v, causal=False, scale=None, signs=None, stream=None):
         scale = d ** -0.5
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    q8, qe = fp8_quantize(q, signs=signs, stream=stream)
+    q8, qe = fp8_quantize(q, signs=signs, stream=stream, scale=scale)
     k8, ke = fp8_quantize(k, signs=signs, stream=stream)
     vt8, ve = fp8_quantize(v, transpose=True, stream=stream)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    attn_fwd_fp8(q8, k8, vt8, qe, ke, ve, o, lse, B, H, N, d, causal, scale, signs is not None, stream)
+    attn_fwd_fp8(q8, k8, vt8, qe, ke, ve, o, lse, B, H, N, d, causal, stream)
     return o, lse

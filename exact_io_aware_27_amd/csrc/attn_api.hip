@@ -8,6 +8,7 @@
 #include <mutex>
 
 #include "../../include/attn.h"
+#include "attn_common.h"
 #include "attn_launch.h"
 
 namespace {
@@ -323,8 +324,10 @@ extern "C" int attn_bwd(const void *q, const void *k, const void *v, const void 
 
 extern "C" int64_t attn_fp8_padded_rows(int64_t N) { return N < 0 ? -1 : attn_fp8_rows(N); }
 
-extern "C" int attn_fp8_quantize(const void *x, int64_t B, int64_t H, int64_t N, int64_t d, int transpose,
-                                 const uint32_t *sign_bits, void *out, void *exps, void *stream)
+// attn_fp8_quantize and attn_fp8_quantize_q: `scale` is null for the first
+// (no multiplier), else the softmax scale of Q's call.
+static int fp8_quantize(const void *x, int64_t B, int64_t H, int64_t N, int64_t d, int transpose,
+                        const uint32_t *sign_bits, const float *scale, void *out, void *exps, void *stream)
 {
     int64_t BH, rows, np_rows, bytes, xbytes, nexp;
     if (B < 0 || H < 0 || N < 0 || !mul_ok(B, H, &BH) || !mul_ok(BH, N, &rows))
@@ -338,6 +341,8 @@ extern "C" int attn_fp8_quantize(const void *x, int64_t B, int64_t H, int64_t N,
     nexp = np_rows / 64;
     if (transpose && sign_bits)  // V is not rotated
         return ATTN_BAD_ARGUMENT;
+    if (scale && !std::isfinite(*scale))
+        return ATTN_BAD_SCALE;
     if (rows == 0)
         return ATTN_OK;
     if (!x || !out || !exps)
@@ -352,6 +357,15 @@ extern "C" int attn_fp8_quantize(const void *x, int64_t B, int64_t H, int64_t N,
     q.exps = exps;
     q.sign_bits = sign_bits;
     q.transpose = transpose != 0;
+    // Q's logits in log2 units: scale * log2(e), and 1/d when Q and K are
+    // rotated (their product then carries the Hadamard factor d); one fp32
+    // product, then an exact power of two.
+    q.mul = 1.f;
+    if (scale) {
+        q.mul = *scale * attn_gfx950::kLog2e;
+        if (sign_bits)
+            q.mul *= 1.f / static_cast<float>(d);
+    }
     q.BH = BH;
     q.N = N;
     q.stream = static_cast<hipStream_t>(stream);
@@ -363,9 +377,21 @@ extern "C" int attn_fp8_quantize(const void *x, int64_t B, int64_t H, int64_t N,
     return ATTN_OK;
 }
 
+extern "C" int attn_fp8_quantize(const void *x, int64_t B, int64_t H, int64_t N, int64_t d, int transpose,
+                                 const uint32_t *sign_bits, void *out, void *exps, void *stream)
+{
+    return fp8_quantize(x, B, H, N, d, transpose, sign_bits, nullptr, out, exps, stream);
+}
+
+extern "C" int attn_fp8_quantize_q(const void *x, int64_t B, int64_t H, int64_t N, int64_t d,
+                                   const uint32_t *sign_bits, float scale, void *out, void *exps, void *stream)
+{
+    return fp8_quantize(x, B, H, N, d, 0, sign_bits, &scale, out, exps, stream);
+}
+
 extern "C" int attn_fwd_fp8(const void *q8, const void *k8, const void *vt8, const void *q_exps, const void *k_exps,
                             const void *v_exps, void *o, float *lse, int64_t B, int64_t H, int64_t N, int64_t d,
-                            int causal, float scale, int rotated, void *stream)
+                            int causal, void *stream)
 {
     int64_t BH, rows, np_rows, bytes, obytes, lse_bytes, nexp;
     if (B < 0 || H < 0 || N < 0 || !mul_ok(B, H, &BH) || !mul_ok(BH, N, &rows))
@@ -378,8 +404,6 @@ extern "C" int attn_fwd_fp8(const void *q8, const void *k8, const void *vt8, con
         attn_workgroups(BH, N, N, 1) > INT32_MAX)
         return ATTN_BAD_SHAPE;
     nexp = np_rows / 64;
-    if (!std::isfinite(scale))
-        return ATTN_BAD_SCALE;
     if (rows == 0)
         return ATTN_OK;
     if (!q8 || !k8 || !vt8 || !q_exps || !k_exps || !v_exps || !o)
@@ -406,9 +430,6 @@ extern "C" int attn_fwd_fp8(const void *q8, const void *k8, const void *vt8, con
     a.BH = BH;
     a.N = N;
     a.causal = causal != 0;
-    // Q and K rotated by the same random-sign Hadamard matrix (+-1 entries,
-    // no 1/sqrt(d)) multiply their product by d: divide it out of the scale.
-    a.scale = rotated ? scale / static_cast<float>(d) : scale;
     a.stream = static_cast<hipStream_t>(stream);
     const hipError_t err = attn_fp8_launch(a);
     if (err != hipSuccess) {

@@ -18,8 +18,12 @@
 //   * Incoherent processing: x -> (x * s) H, random signs s, then the
 //     Sylvester Hadamard matrix H by its fast transform in fp32 (butterfly
 //     stages of stride 1, 2, ..., 64, each (a, b) -> (a + b, a - b)).  The
-//     product of rotated Q and K is d times the original: attn_fwd_fp8
-//     divides d out of the softmax scale when told the inputs are rotated.
+//     product of rotated Q and K is d times the original.
+//   * Q alone is then multiplied in fp32 by c = scale * log2(e) (and 1/d when
+//     rotated) before it is quantized, so that Q K^T comes out of the matrix
+//     cores as the logits in log2 units: the attention kernel applies no
+//     scale, and it starts every score product from the negated reference
+//     max in the accumulator, so that p = exp2 of the product's result.
 //   * Q and K: [BH][Np][128] bytes, Np = N rounded up to 64, rows past N zero.
 //     V: transposed, [BH][128][Np], and within every 64-key tile the keys are
 //     stored in the order the P operand of the P V product holds them: key r
@@ -33,7 +37,8 @@
 // 32-key halves, two K = 64 MFMAs each), the softmax against a lagging
 // reference max, and O^T += V^T P^T (four MFMAs over the block's 64 keys).
 // The softmax of block s runs while the matrix cores compute S of block s+1
-// and P V of block s-1; K and V are copied two blocks ahead of their use.  P is rounded to E4M3
+// (minus the reference, taken in the accumulator) and P V of block s-1; K
+// and V are copied two blocks ahead of their use.  P is rounded to E4M3
 // for the product (the reference may lag the row max by at most 8 in log2
 // units, so P <= 256 stays inside E4M3); O is divided by the fp32 sum of the
 // unrounded P, which also gives the LSE.
@@ -117,13 +122,15 @@ __device__ __forceinline__ float row_butterfly(float v, float sign)
 // columns 8 (t % 16) .. +7 of four rows: rows 16 p + t / 16 (p = 0..3), or,
 // for the transposed V, the consecutive rows 4 (t / 16) + p.  ROTATE applies
 // the signs and the fast Hadamard transform (three stages inside a thread,
-// four across the 16 lanes of a row, through DPP moves); TRANSPOSE converts
+// four across the 16 lanes of a row, through DPP moves), then every value is
+// multiplied by `mul` in fp32 (1 leaves it as it is; Q takes the softmax
+// scale in log2 units); TRANSPOSE converts
 // column by column (the four rows of one column are four consecutive bytes of
 // the tile's key order) and writes V^T through LDS.
 template <bool ROTATE, bool TRANSPOSE>
 __global__ __launch_bounds__(256) void quantize_kernel(const __bf16 *__restrict__ x, uint8_t *__restrict__ out,
                                                        uint8_t *__restrict__ exps, int N, int Np, int nblk,
-                                                       uint32_t s0, uint32_t s1, uint32_t s2, uint32_t s3)
+                                                       uint32_t s0, uint32_t s1, uint32_t s2, uint32_t s3, float mul)
 {
     __shared__ float wmax[4];
     // V^T staging: column c's 64 key bytes at 64 c, 16-byte chunk q of it at
@@ -172,8 +179,10 @@ __global__ __launch_bounds__(256) void quantize_kernel(const __bf16 *__restrict_
             }
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
+        for (int e = 0; e < 8; ++e) {
+            v[p][e] *= mul;
             amax = fmaxf(amax, fabsf(v[p][e]));
+        }
     }
 #pragma unroll
     for (int m = 1; m < 64; m *= 2)
@@ -233,7 +242,6 @@ struct F8Args {
     __bf16 *O;                        // [BH][N][128]
     float *LSE;                       // [BH][N] or null
     int BH, N, Np, nblk, n_wg, nqt;
-    float c_log2;
 };
 
 __device__ __forceinline__ f32x16 mfma8(const i32x8 &a, const i32x8 &b, const f32x16 &c, int sa, int sb)
@@ -258,11 +266,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     __shared__ __attribute__((aligned(1024))) char sk1[kTileBytes];
     __shared__ __attribute__((aligned(1024))) char sv0[kTileBytes];
     __shared__ __attribute__((aligned(1024))) char sv1[kTileBytes];
+    // Each thread's pending rescale factor (set when its row's reference
+    // moves, applied to O after the next P V): only the rare paths touch it,
+    // so it waits here rather than in a register.
+    __shared__ float s_alpha[kThreads];
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int wave_u = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int N = a.N, Np = a.Np, nqt = a.nqt;
-    const float c_log2 = a.c_log2;
 
     const int n_units = CAUSAL ? (nqt + 1) / 2 : nqt;
     int bh, unit;
@@ -296,15 +307,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         // S operand: row n of a 32-key block, bytes 64 st + 32 half .. +31
         // (chunks 4 st + 2 half + c).  P V operand of block b64 of a tile: V^T
         // row n of a 32-row block, bytes 64 b64 + 32 half .. +31 (chunks
-        // 4 b64 + 2 half + c).  Both swizzles repeat every 16 rows.
-        uint32_t koff[2][2], voff[2][2];
+        // 4 b64 + 2 half + c).  Both swizzles repeat every 16 rows, so the
+        // two operands share one set of offsets (koff[b64][c] for V^T).
+        uint32_t koff[2][2];
 #pragma unroll
         for (int st = 0; st < 2; ++st)
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
+            for (int c = 0; c < 2; ++c)
                 koff[st][c] = (uint32_t)(n * kD + (((4 * st + 2 * half + c) ^ swz_k(n)) << 4));
-                voff[st][c] = (uint32_t)(n * kD + (((4 * st + 2 * half + c) ^ swz_k(n)) << 4));
-            }
         const int q0 = qt * kBr;
         const int qw0 = q0 + 32 * wave_u;
         const int qidx = qw0 + n;
@@ -366,11 +376,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
 
-        // Scores of 64-key block b64 of the tile in K buffer kbuf.
-        auto scores = [&](const char *kbuf, int b64, int ks, f32x16 *s) __attribute__((always_inline)) {
+        // Scores of 64-key block b64 of the tile in K buffer kbuf, in log2
+        // units (Q was quantized with the softmax scale and log2 e folded in),
+        // added to `init`: the reference max is subtracted in the matrix
+        // product's accumulator, so p = exp2 of the result with no VALU work.
+        auto scores = [&](const char *kbuf, int b64, int ks, f32x16 *s, const f32x16 &init)
+            __attribute__((always_inline)) {
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
-                s[b] = f32x16{};
+                s[b] = init;
 #pragma unroll
                 for (int st = 0; st < 2; ++st)
                     s[b] = mfma8(lds_pair(kbuf + (64 * b64 + 32 * b) * kD + koff[st][0],
@@ -379,7 +393,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             }
         };
         f32x16 sc[2];
-        scores(sk0, 0, exp_of(a.ke, 0), sc);
+        scores(sk0, 0, exp_of(a.ke, 0), sc, f32x16{});
 
         // Register 4 j + e of 32-key half b holds key 64 s + 32 b + 8 j + 4 half + e
         // of 64-key block s.
@@ -387,20 +401,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             const int key = 64 * blk + 32 * b + 8 * (r >> 2) + 4 * half + (r & 3);
             return key < N && (!CAUSAL || key <= qidx);
         };
-        float m_ref, m_sub, m_thr;
+        // The reference max m (log2 units) lives in neg_m, which holds -m in
+        // every register (0 while the row has seen no key, m = -inf): the
+        // accumulator every score product starts from, so scores arrive
+        // relative to the reference.  A row whose next block passes m_thr
+        // (kRefSlack; -inf while no key was seen) moves the reference.
+        float m_thr;
+        f32x16 neg_m;
         auto set_ref = [&](float m) __attribute__((always_inline)) {
-            m_ref = m;
-            m_sub = (m == kNegInf) ? 0.f : m;
-            m_thr = m + kRefSlack;
+            m_thr = (m == kNegInf) ? kNegInf : kRefSlack;
+            const float m_sub = (m == kNegInf) ? 0.f : m;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                neg_m[r] = -m_sub;
         };
+        auto ref_sub = [&]() __attribute__((always_inline)) { return -neg_m[0]; };
+        auto ref_max = [&]() __attribute__((always_inline)) { return m_thr == kNegInf ? kNegInf : -neg_m[0]; };
         {
             float mx = kNegInf;
 #pragma unroll
             for (int b = 0; b < 2; ++b)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    mx = fmaxf(mx, visible(0, b, r) ? sc[b][r] * c_log2 : kNegInf);
+                    mx = fmaxf(mx, visible(0, b, r) ? sc[b][r] : kNegInf);
             set_ref(wave_half_max(mx));
+            // the first block's scores were formed before the reference existed
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+                sc[b] += neg_m;
         }
         f32x16 oacc[4];
 #pragma unroll
@@ -408,7 +436,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             oacc[b] = f32x16{};
         float l_run = 0.f;
         bool pending = false;
-        float alpha_pend = 1.f;
+        // This thread's slot of s_alpha, its lane index computed afresh where
+        // it is used (from an opaque all-ones mask, so that it is neither
+        // hoisted nor kept live through the key loop for the rare paths).
+        auto alpha_slot = [&]() __attribute__((always_inline)) -> float & {
+            uint32_t all = ~0u;
+            asm volatile("" : "+s"(all));
+            const int l = (int)__builtin_amdgcn_mbcnt_hi(all, __builtin_amdgcn_mbcnt_lo(all, 0u));
+            return s_alpha[wave_u * kWave + l];
+        };
         i32x8 pb_prev = i32x8{};
         // Block exponents, loaded one step ahead of their use, so that no
         // scalar load's latency sits in front of a step's first MFMA (the
@@ -452,7 +488,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             // softmax inside its step.
 #pragma unroll
             for (int st = 0; st < 2; ++st)
-                asm volatile("" : "+v"(koff[st][0]), "+v"(koff[st][1]), "+v"(voff[st][0]), "+v"(voff[st][1]));
+                asm volatile("" : "+v"(koff[st][0]), "+v"(koff[st][1]));
             asm volatile("" : "+v"(sc[0]), "+v"(sc[1]));
 
             // P of block s against the reference, rounded to E4M3 in the order
@@ -463,7 +499,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             for (int b = 0; b < 2; ++b)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    p[b][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[b][r], c_log2, -m_sub));
+                    p[b][r] = __builtin_amdgcn_exp2f(sc[b][r]);
                     if constexpr (MASKED)
                         p[b][r] = visible(blk, b, r) ? p[b][r] : 0.f;
                 }
@@ -490,11 +526,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             }
 
             f32x16 sn[2];
-            scores(knext, knext_b64, ks, sn);
+            scores(knext, knext_b64, ks, sn, neg_m);
 #pragma unroll
             for (int db = 0; db < 4; ++db)
-                oacc[db] = mfma8(lds_pair(vprev + db * 32 * kD + voff[vprev_b64][0],
-                                          vprev + db * 32 * kD + voff[vprev_b64][1]),
+                oacc[db] = mfma8(lds_pair(vprev + db * 32 * kD + koff[vprev_b64][0],
+                                          vprev + db * 32 * kD + koff[vprev_b64][1]),
                                  pb_prev, oacc[db], vs, kE8M0One);
 
             float mx;
@@ -504,24 +540,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 for (int b = 0; b < 2; ++b)
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
-                        mx = fmaxf(mx, visible(blk + 1, b, r) ? sn[b][r] * c_log2 : kNegInf);
-            } else {  // every key visible and c_log2 > 0
+                        mx = fmaxf(mx, visible(blk + 1, b, r) ? sn[b][r] : kNegInf);
+            } else {  // every key visible
                 float m0 = sn[0][0];
 #pragma unroll
                 for (int r = 1; r < 32; ++r)
                     m0 = fmaxf(m0, sn[r >> 4][r & 15]);
-                mx = m0 * c_log2;
+                mx = m0;
             }
             const bool reref = __builtin_amdgcn_ballot_w64(mx > m_thr) != 0;
 
             // The step's region: 8 MFMAs, each followed by the operand reads
             // for the MFMAs after it and a share of the softmax VALU work.
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+            // (Not in the masked steps without the causal mask, which only
+            // the ragged end of a sequence runs: left to the default
+            // scheduler, they fit the register budget.)
+            if constexpr (CAUSAL || !MASKED) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // reads before the VALU share: 1.8% faster
-                __builtin_amdgcn_sched_group_barrier(0x402, 16, 0);
+                for (int i = 0; i < 8; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // reads before the VALU share: 1.8% faster
+                    __builtin_amdgcn_sched_group_barrier(0x400, 4, 0);   // exp
+                    __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // other VALU
+                }
             }
             asm volatile("" : "+v"(pb), "+v"(l_run));
 
@@ -530,14 +572,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             if (__builtin_expect(pending, 0)) {
 #pragma unroll
                 for (int b = 0; b < 4; ++b)
-                    oacc[b] *= alpha_pend;
+                    oacc[b] *= alpha_slot();
             }
             pending = reref;
             if (__builtin_expect(reref, 0)) {
-                const float m_new = fmaxf(m_ref, wave_half_max(mx));
-                alpha_pend = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-                l_run *= alpha_pend;
+                const float m_old = ref_sub(), m_ref = ref_max();
+                const float m_new = fmaxf(m_ref, wave_half_max(mx + m_old));
+                const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+                alpha_slot() = alpha;
+                l_run *= alpha;
                 set_ref(m_new);
+                // the next block's scores were formed against the old reference
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+                    sn[b] -= (ref_sub() - m_old);
             }
             sc[0] = sn[0];
             sc[1] = sn[1];
@@ -557,15 +605,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         using Unmasked = std::false_type;
         using Masked = std::true_type;
         // Blocks [0, b_free) need no mask: inside the sequence and at or below
-        // the causal diagonal of every query of the workgroup (and a positive
-        // scale, which the unmasked row max assumes).  Whole unmasked tile
-        // pairs run in the first loop; the last one is peeled because the block
-        // after it needs the mask.
+        // the causal diagonal of every query of the workgroup.  Whole unmasked
+        // tile pairs run in the first loop; the last one is peeled because the
+        // block after it needs the mask.
         int b_free = N / kRowsBlk;
         if (CAUSAL)
             b_free = min(b_free, (q0 + 1) / kRowsBlk);
-        if (!(c_log2 > 0.f))
-            b_free = 0;
         b_free = min(b_free, nb_end);
         const int t_free = (b_free / 2) & ~1;  // unmasked tiles, an even count
         int t = 0;
@@ -591,12 +636,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             const int vs = vs_next;
 #pragma unroll
             for (int db = 0; db < 4; ++db)
-                oacc[db] = mfma8(lds_pair(vlast + db * 32 * kD + voff[1][0], vlast + db * 32 * kD + voff[1][1]),
+                oacc[db] = mfma8(lds_pair(vlast + db * 32 * kD + koff[1][0], vlast + db * 32 * kD + koff[1][1]),
                                  pb_prev, oacc[db], vs, kE8M0One);
             if (__builtin_expect(pending, 0)) {
 #pragma unroll
                 for (int b = 0; b < 4; ++b)
-                    oacc[b] *= alpha_pend;
+                    oacc[b] *= alpha_slot();
             }
             // O is read only by the lanes of valid queries: keep these MFMAs
             // out of that lane-masked branch (an MFMA under a partial EXEC mask
@@ -620,7 +665,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                     *reinterpret_cast<u32x2 *>(orow + 32 * b + 8 * j + 4 * half) = w;
                 }
             if (a.LSE != nullptr && half == 0)
-                a.LSE[(size_t)bh * N + qidx] = (m_ref + __builtin_log2f(l_tot)) * 0.69314718055994530942f;
+                a.LSE[(size_t)bh * N + qidx] = (ref_max() + __builtin_log2f(l_tot)) * 0.69314718055994530942f;
         }
     }
 #endif
@@ -642,13 +687,13 @@ hipError_t attn_fp8_quantize_launch(const AttnFp8Quantize &q)
     uint8_t *out = (uint8_t *)q.out, *exps = (uint8_t *)q.exps;
     if (q.transpose)
         hipLaunchKernelGGL((quantize_kernel<false, true>), dim3(grid), dim3(256), 0, q.stream, x, out, exps, (int)q.N, Np,
-                           nblk, 0u, 0u, 0u, 0u);
+                           nblk, 0u, 0u, 0u, 0u, 1.f);
     else if (s)
         hipLaunchKernelGGL((quantize_kernel<true, false>), dim3(grid), dim3(256), 0, q.stream, x, out, exps, (int)q.N, Np,
-                           nblk, s0, s1, s2, s3);
+                           nblk, s0, s1, s2, s3, q.mul);
     else
         hipLaunchKernelGGL((quantize_kernel<false, false>), dim3(grid), dim3(256), 0, q.stream, x, out, exps, (int)q.N, Np,
-                           nblk, 0u, 0u, 0u, 0u);
+                           nblk, 0u, 0u, 0u, 0u, q.mul);
     return hipGetLastError();
 }
 
@@ -670,7 +715,6 @@ hipError_t attn_fp8_launch(const AttnFp8Launch &l)
     a.nblk = a.Np / kRowsBlk;
     a.nqt = (int)((l.N + kBr - 1) / kBr);
     a.n_wg = (int)(l.BH * (l.causal ? (a.nqt + 1) / 2 : a.nqt));
-    a.c_log2 = l.scale * attn_gfx950::kLog2e;
     if (l.causal)
         hipLaunchKernelGGL((attn_fwd_fp8_kernel<true>), dim3(a.n_wg), dim3(kThreads), 0, l.stream, a);
     else

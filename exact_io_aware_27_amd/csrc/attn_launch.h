@@ -69,6 +69,7 @@ struct AttnFp8Quantize {
     void *out, *exps;            // FP8 bytes and E8M0 block exponents
     const uint32_t *sign_bits;   // host, 4 words, or null (no rotation)
     bool transpose;              // V^T layout (no rotation)
+    float mul;                   // fp32 multiplier after the rotation (1: none)
     int64_t BH, N;
     hipStream_t stream;
 };
@@ -81,7 +82,6 @@ struct AttnFp8Launch {
     float *lse;
     int64_t BH, N;
     bool causal;
-    float scale;
     hipStream_t stream;
 };
 hipError_t attn_fp8_launch(const AttnFp8Launch &a);

@@ -241,7 +241,8 @@ ATTN_API int64_t attn_fp8_padded_rows(int64_t N);
  * rotated, x -> (x * s) H with H the 128 x 128 Sylvester Hadamard matrix
  * (+-1 entries, no 1/sqrt(128)), computed in fp32 by the fast transform with
  * strides 1, 2, ..., 64.  Q and K rotated with the same signs keep their
- * product times 128; attn_fwd_fp8 with rotated != 0 divides it out.  Errors:
+ * product times 128 (attn_fp8_quantize_q divides it out of Q).  This call
+ * quantizes K and V for attn_fwd_fp8 (Q: attn_fp8_quantize_q).  Errors:
  * BAD_SHAPE, UNSUPPORTED_D (d != 128), BAD_ARGUMENT (signs with transpose),
  * (empty -> OK), NULL_PTR, MISALIGNED, ALIAS.  One kernel on `stream`.
  */
@@ -249,22 +250,34 @@ ATTN_API int attn_fp8_quantize(const void *x, int64_t B, int64_t H, int64_t N, i
                       const uint32_t *sign_bits, void *out, void *exps, void *stream);
 
 /*
+ * attn_fp8_quantize_q -- Q's quantization for attn_fwd_fp8: attn_fp8_quantize
+ * with transpose == 0, except that after the rotation every value is
+ * multiplied in fp32 by c = scale * log2(e) (one fp32 product), and by a
+ * further 1/128 when sign_bits is given (the rotated Q K product carries the
+ * Hadamard factor 128).  Q K^T of the quantized operands is then the logits
+ * scale * q . k in log2 units, which attn_fwd_fp8 takes as they are.  scale
+ * is the softmax scale of the original (unrotated) Q and K, e.g.
+ * 1/sqrt(128); any finite value, zero and negative included.  Errors as
+ * attn_fp8_quantize, and BAD_SCALE for a scale that is not finite.
+ */
+ATTN_API int attn_fp8_quantize_q(const void *x, int64_t B, int64_t H, int64_t N, int64_t d,
+                        const uint32_t *sign_bits, float scale, void *out, void *exps, void *stream);
+
+/*
  * attn_fwd_fp8 -- O (bf16 [B][H][N][128]) and LSE (fp32 [B][H][N] or NULL)
- * of softmax(scale * Q K^T) V from the FP8 operands attn_fp8_quantize
- * produced (q8, k8 rows; vt8 transposed; their exponent arrays).  Both
- * products run on the FP8 matrix cores with the block scales applied by the
- * hardware; P is rounded to E4M3 for the P V product and O is divided by the
- * fp32 sum of the unrounded P.  scale is the softmax scale of the original
- * (unrotated) Q and K, e.g. 1/sqrt(128).  rotated: nonzero when q8 and k8
- * were quantized with the same sign_bits (incoherent processing): their
- * product then carries the Hadamard factor 128, which the call divides out
- * of scale itself.  causal, stream as attn_fwd.  Errors as attn_fwd
+ * of softmax(scale * Q K^T) V from the FP8 operands: q8 and q_exps from
+ * attn_fp8_quantize_q (which folds the softmax scale, log2(e) and the
+ * rotation's factor into Q), k8 and vt8 (transposed) and their exponents
+ * from attn_fp8_quantize, Q and K rotated with the same sign_bits or both
+ * not rotated (incoherent processing).  Both products run on the FP8 matrix
+ * cores with the block scales applied by the hardware; P is rounded to E4M3
+ * for the P V product and O is divided by the fp32 sum of the unrounded P.
+ * causal, stream as attn_fwd.  Errors as attn_fwd without BAD_SCALE
  * (d != 128 is UNSUPPORTED_D); one kernel on `stream`.
  */
 ATTN_API int attn_fwd_fp8(const void *q8, const void *k8, const void *vt8, const void *q_exps,
                  const void *k_exps, const void *v_exps, void *o, float *lse,
-                 int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
-                 int rotated, void *stream);
+                 int64_t B, int64_t H, int64_t N, int64_t d, int causal, void *stream);
 
 /* Static, human-readable name of a status code ("ATTN_OK", ...). */
 ATTN_API const char *attn_status_string(int status);

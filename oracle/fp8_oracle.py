@@ -28,6 +28,13 @@ section).  The readings taken here where they are silent:
     quantized, so the rotation's fp32 roundings decide FP8 codes; they are
     taken in fp32 here, in this order, as in the kernel.
   * V is quantized in blocks of 64 keys without rotation.
+  * Q alone is multiplied, after its rotation and before it is quantized, by
+    c = scale * log2(e) in fp32 (one fp32 product of the fp32 scale and
+    log2(e) rounded to fp32, then 1/d when rotated, exact), so that the
+    product of the quantized operands is the logits in log2 units.  The pages
+    do not say where the softmax scale enters the FP8 products; here it rides
+    with Q's quantization, whose relative rounding error does not depend on
+    the magnitude of what it rounds.
 
 Parity unpinned: the size of the pages' FP8 error reduction (2.6x against
 per-tensor FP8).  The pages give no input distribution for it; on the
@@ -148,15 +155,20 @@ def dequantize(codes, exps, block=BLOCK):
     return codes * scale[..., None]
 
 
-def prepare_fp8(q, k, v, signs=None, per_tensor=False):
+def prepare_fp8(q, k, v, signs=None, per_tensor=False, scale=None):
     """Quantize bf16/float q, k, v [B, H, N, d] the way the FP8 path does.
 
     signs: None (no incoherent processing) or +-1 float array [d]: Q and K are
     rotated by fwht_f32(x * signs) first (their product gains the factor d).
     per_tensor: one exponent per tensor instead of per 64-row block.
+    scale: None, or the softmax scale: Q (after the rotation) is then
+    multiplied in fp32 by c = fp32(scale) * fp32(log2 e), times 1/d when
+    rotated, before it is quantized.
     Returns a dict of dequantized float64 tensors 'q', 'k', 'v', the codes
-    'qc', 'kc', 'vc', the exponents 'qe', 'ke', 've', and 'qk_factor' (the
-    factor the product QK^T gained: d with rotation, else 1).
+    'qc', 'kc', 'vc', the exponents 'qe', 'ke', 've', 'qk_factor' (the
+    factor the product QK^T gained: d with rotation, else 1) and 'qk_mul'
+    (with scale: ln 2, which turns the product of the dequantized operands
+    into natural-log logits; else None).
     """
     def f32(x):
         import torch
@@ -168,7 +180,13 @@ def prepare_fp8(q, k, v, signs=None, per_tensor=False):
         s = np.asarray(signs, dtype=np.float32)
         qf = fwht_f32(qf * s)
         kf = fwht_f32(kf * s)
-    out = {"qk_factor": float(d) if signs is not None else 1.0}
+    if scale is not None:
+        c = np.float32(scale) * np.float32(np.log2(np.e))
+        if signs is not None:
+            c = c * np.float32(1.0 / d)
+        qf = (qf * c).astype(np.float32)
+    out = {"qk_factor": float(d) if signs is not None else 1.0,
+           "qk_mul": float(np.log(2.0)) if scale is not None else None}
     for name, x in (("q", qf), ("k", kf), ("v", vf)):
         if per_tensor:
             c, E = tensor_quantize(x)
@@ -209,13 +227,14 @@ def attention_fp64(q, k, v, causal, scale, p_rounding=False):
     return o, lse, sigma
 
 
-def attention_fp8(prep, causal, scale):
+def attention_fp8(prep, causal, scale=None):
     """FP8 attention of a prepare_fp8() result: S from the dequantized Q and
-    K (scale / qk_factor undoes the rotation's factor d), P = exp(S - max)
-    rounded to E4M3, O = P' V / sum P, LSE from the unrounded sum.
-    Returns (o, lse) float64."""
+    K (times qk_mul when Q carries the scale, else scale / qk_factor, which
+    undoes the rotation's factor d), P = exp(S - max) rounded to E4M3,
+    O = P' V / sum P, LSE from the unrounded sum.  Returns (o, lse) float64."""
     q, k, v = prep["q"], prep["k"], prep["v"]
-    s = (scale / prep["qk_factor"]) * np.einsum("bhid,bhjd->bhij", q, k)
+    mul = prep["qk_mul"] if prep.get("qk_mul") is not None else scale / prep["qk_factor"]
+    s = mul * np.einsum("bhid,bhjd->bhij", q, k)
     Nq, Nk = q.shape[2], k.shape[2]
     if causal:
         s = np.where(np.tril(np.ones((Nq, Nk), dtype=bool), Nk - Nq), s, -np.inf)

@@ -32,7 +32,7 @@ def test_header_declares_the_abi():
     assert set(_declared()) == {"attn_fwd", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_bytes",
                                 "attn_fwd_splitkv_noalloc", "attn_noalloc_scratch_bytes",
                                 "attn_bwd", "attn_bwd_workspace_bytes", "attn_fp8_padded_rows",
-                                "attn_fp8_quantize", "attn_fwd_fp8", "attn_status_string",
+                                "attn_fp8_quantize", "attn_fp8_quantize_q", "attn_fwd_fp8", "attn_status_string",
                                 "attn_last_hip_error"}
 
 
@@ -198,9 +198,12 @@ def _quant(lib, x=Q, B=2, H=3, N=100, d=128, tr=0, signs=None, out=O, ex=L):
     return lib.attn_fp8_quantize(x, B, H, N, d, tr, signs, out, ex, None)
 
 
-def _fp8(lib, q=Q, k=K, v=V, qe=W, ke=W + 4096, ve=W + 8192, o=O, lse=L, B=2, H=3, N=100, d=128, causal=1,
-         scale=0.1, rotated=1):
-    return lib.attn_fwd_fp8(q, k, v, qe, ke, ve, o, lse, B, H, N, d, causal, scale, rotated, None)
+def _quant_q(lib, x=Q, B=2, H=3, N=100, d=128, signs=None, scale=0.1, out=O, ex=L):
+    return lib.attn_fp8_quantize_q(x, B, H, N, d, signs, scale, out, ex, None)
+
+
+def _fp8(lib, q=Q, k=K, v=V, qe=W, ke=W + 4096, ve=W + 8192, o=O, lse=L, B=2, H=3, N=100, d=128, causal=1):
+    return lib.attn_fwd_fp8(q, k, v, qe, ke, ve, o, lse, B, H, N, d, causal, None)
 
 
 def test_fp8_argument_errors_before_any_hip_call(lib):
@@ -215,7 +218,11 @@ def test_fp8_argument_errors_before_any_hip_call(lib):
     assert _quant(lib, x=None) == 1 and _quant(lib, ex=None) == 1
     assert _quant(lib, x=Q + 8) == 5 and _quant(lib, out=O + 4) == 5
     assert _quant(lib, out=Q + 64) == 6 and _quant(lib, ex=Q) == 6
-    assert _fp8(lib, N=-1) == 2 and _fp8(lib, d=64) == 3 and _fp8(lib, scale=float("nan")) == 4
+    assert _quant_q(lib, B=-1) == 2 and _quant_q(lib, d=64) == 3
+    assert _quant_q(lib, scale=float("nan")) == 4 and _quant_q(lib, scale=float("inf"), signs=bits) == 4
+    assert _quant_q(lib, N=0, x=None) == 0 and _quant_q(lib, x=None) == 1
+    assert _quant_q(lib, out=O + 4) == 5 and _quant_q(lib, ex=Q) == 6
+    assert _fp8(lib, N=-1) == 2 and _fp8(lib, d=64) == 3
     assert _fp8(lib, B=0, q=None) == 0
     assert _fp8(lib, q=None) == 1 and _fp8(lib, ve=None) == 1 and _fp8(lib, o=None) == 1
     assert _fp8(lib, k=K + 8) == 5 and _fp8(lib, lse=L + 1) == 5

@@ -1,9 +1,10 @@
-"""FP8 forward path (attn_fp8_quantize, attn_fwd_fp8) against the FP8
-oracle (oracle/fp8_oracle.py), on a GPU.
+"""FP8 forward path (attn_fp8_quantize, attn_fp8_quantize_q, attn_fwd_fp8)
+against the FP8 oracle (oracle/fp8_oracle.py), on a GPU.
 
   * Quantization is byte work: the codes and exponents must equal the
-    oracle's bit for bit (the rotation's fp32 roundings are taken in the same
-    order on both sides).
+    oracle's bit for bit (the rotation's fp32 roundings, and Q's fp32
+    multiplication by the scale in log2 units, are taken in the same order on
+    both sides).
   * The attention is compared with exact attention of the dequantized
     operands.  What remains is P's rounding to E4M3 before P V, whose size the
     oracle predicts per element (sigma, from the actual P and V), plus one
@@ -50,25 +51,31 @@ def untranspose(vt, N):
     return np.swapaxes(vt[..., pos], -1, -2)
 
 
-@pytest.mark.parametrize("B,H,N,rotate", [(1, 2, 200, False), (1, 2, 200, True), (2, 1, 1, True),
-                                          (1, 1, 64, False), (1, 3, 333, True), (1, 1, 1000, False)])
-def test_quantize_is_bit_exact(B, H, N, rotate):
+@pytest.mark.parametrize("B,H,N,rotate,scale", [(1, 2, 200, False, 0.0884), (1, 2, 200, True, 0.0884),
+                                                (2, 1, 1, True, 1.0), (1, 1, 64, False, -0.3),
+                                                (1, 3, 333, True, 0.0884), (1, 1, 1000, False, 0.0884)])
+def test_quantize_is_bit_exact(B, H, N, rotate, scale):
+    """The same bf16 tensor as Q (attn_fp8_quantize_q: times the scale in
+    log2 units), as K (attn_fp8_quantize, rotated alike) and as V
+    (transposed), against the oracle's codes and exponents."""
     from exact_io_aware_27_amd import attn
     q, _, v = inputs.make_qkv_outliers(B, H, N, 128, seed=4000 + N, frac=1e-2)
     signs = inputs.make_signs(128, seed=4001).numpy() if rotate else None
-    say("case: quantize", (B, H, N), "rotated" if rotate else "plain")
+    say("case: quantize", (B, H, N), "rotated" if rotate else "plain", "scale", scale)
     qd, vd = q.to(DEV), v.to(DEV)
-    q8, qe = attn.fp8_quantize(qd, signs=signs)
+    q8, qe = attn.fp8_quantize(qd, signs=signs, scale=scale)
+    k8, ke = attn.fp8_quantize(qd, signs=signs)
     vt8, ve = attn.fp8_quantize(vd, transpose=True)
     torch.cuda.synchronize()
-    ref = f8.prepare_fp8(q, q, v, signs=signs)
+    ref = f8.prepare_fp8(q, q, v, signs=signs, scale=scale)
     Np = attn.fp8_padded_rows(N)
-    want_q = np.zeros((B, H, Np, 128))
-    want_q[:, :, :N] = ref["qc"]
+    for name, codes, exps in (("q", q8, qe), ("k", k8, ke)):
+        want = np.zeros((B, H, Np, 128))
+        want[:, :, :N] = ref[name + "c"]
+        np.testing.assert_array_equal(codes_of(codes), want)
+        np.testing.assert_array_equal(exps.cpu().numpy().astype(np.int64) - 127, ref[name + "e"])
     want_v = np.zeros((B, H, Np, 128))
     want_v[:, :, :N] = ref["vc"]
-    np.testing.assert_array_equal(codes_of(q8), want_q)
-    np.testing.assert_array_equal(qe.cpu().numpy().astype(np.int64) - 127, ref["qe"])
     np.testing.assert_array_equal(untranspose(codes_of(vt8), N), want_v)
     np.testing.assert_array_equal(ve.cpu().numpy().astype(np.int64) - 127, ref["ve"])
 
@@ -87,9 +94,9 @@ def check_attention(B, H, N, causal, rotate, seed, outliers=False, what="", qkv=
     say("case:", what, (B, H, N), "causal" if causal else "non-causal", "rotated" if rotate else "plain")
     o, lse = attn.attention_fp8(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, scale=scale, signs=signs)
     torch.cuda.synchronize()
-    prep = f8.prepare_fp8(q, k, v, signs=signs)
-    o_ref, lse_ref, sigma = f8.attention_fp64(prep["q"], prep["k"], prep["v"], causal,
-                                              scale / prep["qk_factor"], p_rounding=True)
+    prep = f8.prepare_fp8(q, k, v, signs=signs, scale=scale)
+    o_ref, lse_ref, sigma = f8.attention_fp64(prep["q"], prep["k"], prep["v"], causal, prep["qk_mul"],
+                                              p_rounding=True)
     og = o.double().cpu().numpy()
     rounding = parity.bf16_half_ulp(np.maximum(np.abs(o_ref), np.abs(og)))
     total = np.sqrt(sigma ** 2 + rounding ** 2 / 3 + (1e-5) ** 2)
@@ -170,9 +177,9 @@ def test_long_causal_shape_sampled_rows():
     torch.cuda.synchronize()
     for b, h in ((0, 3), (1, 30)):
         sl = (slice(b, b + 1), slice(h, h + 1))
-        prep = f8.prepare_fp8(q[sl], k[sl], v[sl], signs=signs)
+        prep = f8.prepare_fp8(q[sl], k[sl], v[sl], signs=signs, scale=w.scale)
         rows = inputs.row_subset(w.N, 96, w.seed, b * w.H + h, (0, w.N - 1)).numpy()
-        o_ref, lse_ref, sigma = _causal_rows(prep, rows, w.scale)
+        o_ref, lse_ref, sigma = _causal_rows(prep, rows)
         og = o[b, h, rows].double().cpu().numpy()[None, None]
         rounding = parity.bf16_half_ulp(np.maximum(np.abs(o_ref), np.abs(og)))
         z = (og - o_ref) / np.sqrt(sigma ** 2 + rounding ** 2 / 3 + 1e-10)
@@ -181,11 +188,11 @@ def test_long_causal_shape_sampled_rows():
         assert np.mean(z ** 2) <= 2.0 and np.abs(z).max() <= 6.0 and dl.max() <= 1e-3
 
 
-def _causal_rows(prep, rows, scale):
-    """Oracle rows of a causal head: each sampled query against its visible
-    prefix of keys."""
+def _causal_rows(prep, rows):
+    """Oracle rows of a causal head (prepared with the softmax scale in Q):
+    each sampled query against its visible prefix of keys."""
     outs = [f8.attention_fp64(prep["q"][:, :, [r]], prep["k"][:, :, :r + 1], prep["v"][:, :, :r + 1], False,
-                              scale / prep["qk_factor"], p_rounding=True) for r in rows]
+                              prep["qk_mul"], p_rounding=True) for r in rows]
     return (np.concatenate([x[0] for x in outs], axis=2), np.concatenate([x[1] for x in outs], axis=2),
             np.concatenate([x[2] for x in outs], axis=2))
 
@@ -203,9 +210,9 @@ def test_very_long_sequence_sampled_rows():
     torch.cuda.synchronize()
     for h in range(H):
         sl = (slice(0, 1), slice(h, h + 1))
-        prep = f8.prepare_fp8(q[sl], k[sl], v[sl], signs=signs)
+        prep = f8.prepare_fp8(q[sl], k[sl], v[sl], signs=signs, scale=scale)
         rows = inputs.row_subset(N, 12, 4400, h, (0, 63, 64, N - 1)).numpy()
-        o_ref, lse_ref, sigma = _causal_rows(prep, rows, scale)
+        o_ref, lse_ref, sigma = _causal_rows(prep, rows)
         og = o[0, h, rows].double().cpu().numpy()[None, None]
         rounding = parity.bf16_half_ulp(np.maximum(np.abs(o_ref), np.abs(og)))
         z = (og - o_ref) / np.sqrt(sigma ** 2 + rounding ** 2 / 3 + 1e-10)
@@ -216,16 +223,18 @@ def test_very_long_sequence_sampled_rows():
 
 @pytest.mark.parametrize("scale", [0.0, -0.05])
 def test_non_positive_scale(scale):
-    """scale <= 0 takes the path where every tile is masked (the unmasked
-    row max assumes a positive scale): the results must still match."""
+    """scale <= 0: Q takes the scale's sign and size in its quantization
+    (zero: all-zero codes, uniform weights), and the kernel's unmasked row
+    max works on the scaled logits whatever their sign."""
     from exact_io_aware_27_amd import attn
     B, H, N, d = 1, 2, 300, 128
     q, k, v = inputs.make_qkv(B, H, N, d, seed=4500)
     say("case: fp8 scale", scale)
     o, lse = attn.attention_fp8(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, scale=scale)
     torch.cuda.synchronize()
-    prep = f8.prepare_fp8(q, k, v)
-    o_ref, lse_ref, sigma = f8.attention_fp64(prep["q"], prep["k"], prep["v"], True, scale, p_rounding=True)
+    prep = f8.prepare_fp8(q, k, v, scale=scale)
+    o_ref, lse_ref, sigma = f8.attention_fp64(prep["q"], prep["k"], prep["v"], True, prep["qk_mul"],
+                                              p_rounding=True)
     og = o.double().cpu().numpy()
     rounding = parity.bf16_half_ulp(np.maximum(np.abs(o_ref), np.abs(og)))
     z = (og - o_ref) / np.sqrt(sigma ** 2 + rounding ** 2 / 3 + 1e-10)
@@ -234,28 +243,22 @@ def test_non_positive_scale(scale):
     assert np.mean(z ** 2) <= 2.0 and np.abs(z).max() <= 6.0 and dl.max() <= 1e-3
 
 
-def test_rotated_flag_divides_the_scale_in_the_library():
-    """attn_fwd_fp8 takes the softmax scale of the original Q and K; with
-    rotated set the library divides the rotation's factor 128 out itself.
-    Through the C ABI: (scale, rotated) gives the same bits as (scale / 128,
-    not rotated), since dividing by a power of two is exact."""
+def test_query_scale_is_one_fp32_product_after_the_rotation():
+    """attn_fp8_quantize_q multiplies Q, after the rotation, by one fp32
+    constant: doubling the scale (exact in fp32) must give the same codes and
+    every nonzero block's exponent one higher; and a rotated Q's constant
+    carries 1/128, so that its attention equals the oracle's with the
+    rotation's factor taken out (the attention tests check that)."""
     from exact_io_aware_27_amd import attn
     B, H, N, d = 1, 2, 300, 128
-    q, k, v = inputs.make_qkv(B, H, N, d, seed=4300)
+    q, _, _ = inputs.make_qkv(B, H, N, d, seed=4300)
     signs = inputs.make_signs(d, seed=4301).numpy()
-    say("case: rotated flag", (B, H, N))
-    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
-    q8, qe = attn.fp8_quantize(qd, signs=signs)
-    k8, ke = attn.fp8_quantize(kd, signs=signs)
-    vt8, ve = attn.fp8_quantize(vd, transpose=True)
-    scale = d ** -0.5
-    outs = []
-    for sc, rot in ((scale, True), (scale / d, False)):
-        o = torch.empty_like(qd)
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=DEV)
-        st = attn.attn_fwd_fp8_status(q8, k8, vt8, qe, ke, ve, o, lse, B, H, N, d, True, sc, rot,
-                                      torch.cuda.current_stream())
-        assert st == 0, st
-        outs.append((o, lse))
-    torch.cuda.synchronize()
-    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    say("case: query scale", (B, H, N))
+    qd = q.to(DEV)
+    for sg in (None, signs):
+        c1, e1 = attn.fp8_quantize(qd, signs=sg, scale=0.0884)
+        c2, e2 = attn.fp8_quantize(qd, signs=sg, scale=2 * 0.0884)
+        torch.cuda.synchronize()
+        assert torch.equal(c1, c2)
+        nonzero = (c1.view(B, H, -1, 64, d) != 0).any(dim=-1).any(dim=-1)
+        assert torch.equal((e2.long() - e1.long())[nonzero], torch.ones_like(e1.long())[nonzero])

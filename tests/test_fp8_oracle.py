@@ -10,6 +10,10 @@
   P-rounding noise     -> the actual E4M3 rounding of P, measured
   tensor_quantize      -> a hand-worked tensor (exponent, codes, boundary)
   attention_fp8        -> a hand-worked row whose P rounds to known E4M3 codes
+  Q's scale in log2    -> a scale whose fp32 constant is exactly 2^-3: the
+                          same codes, exponents 3 lower (10 when rotated), K
+                          and V untouched, and attention equal to the
+                          unscaled preparation's at scale ln 2 / 8
   the pages' claim     -> block quantization with incoherent processing has
                           lower error than per-tensor FP8 on outlier-heavy input
                           (direction only: the pages' 2.6x comes with no input
@@ -187,3 +191,30 @@ def test_attention_fp8_closed_form(shift):
     prep_r = dict(prep, k=k * 2.0, qk_factor=2.0)
     o_r, _ = f8.attention_fp8(prep_r, False, 1.0)
     np.testing.assert_allclose(o_r, o, rtol=1e-12)
+
+
+@pytest.mark.parametrize("rotate", [False, True])
+def test_query_scale_in_log2_units(rotate):
+    """prepare_fp8 with a softmax scale multiplies Q (after the rotation) by
+    fp32(scale) * fp32(log2 e), times 1/d when rotated.  With a scale whose
+    constant is exactly 2^-3 that multiplication is exact, so Q's codes must
+    equal the unscaled ones and its exponents drop by 3 (by 3 + 7 with the
+    rotation's 1/128), K and V must not change, and attention of the scaled
+    preparation (logits = ln 2 times the product) must equal attention of the
+    unscaled one at scale ln 2 / 8.  A multiplier applied to K, a missing
+    1/d, or natural instead of log2 units each break one of these."""
+    scale = np.float32(0.125 / float(np.float32(np.log2(np.e))))
+    assert float(scale * np.float32(np.log2(np.e))) == 0.125
+    q, k, v = inputs.make_qkv(1, 2, 150, 128, seed=4600)
+    signs = inputs.make_signs(128, seed=4601).numpy() if rotate else None
+    plain = f8.prepare_fp8(q, k, v, signs=signs)
+    scaled = f8.prepare_fp8(q, k, v, signs=signs, scale=float(scale))
+    np.testing.assert_array_equal(scaled["qc"], plain["qc"])
+    np.testing.assert_array_equal(scaled["qe"], plain["qe"] - (10 if rotate else 3))
+    for name in ("kc", "ke", "vc", "ve"):
+        np.testing.assert_array_equal(scaled[name], plain[name])
+    for causal in (False, True):
+        o_s, lse_s = f8.attention_fp8(scaled, causal)
+        o_p, lse_p = f8.attention_fp8(plain, causal, math.log(2.0) / 8)
+        np.testing.assert_allclose(o_s, o_p, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(lse_s, lse_p, rtol=1e-12, atol=1e-12)
