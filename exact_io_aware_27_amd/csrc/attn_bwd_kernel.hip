@@ -104,7 +104,7 @@ __device__ __forceinline__ uint32_t lds_off(int r, int c)
 // Kernel arguments.  Q, O, dO, dQ: [BH][N][d]; K, V, dK, dV: [BH][N][d];
 // LSE: [BH][N] (natural log, from the forward pass).  L2 and Dsum, [BH][N]
 // each, are written by the dQ kernel and read by the dK/dV kernel: the LSE in
-// log2 units and D.  c_log2 = scale * log2(e).
+// log2 units and -D.  c_log2 = scale * log2(e).
 struct BArgs {
     const __bf16 *Q, *K, *V, *O, *dO;
     const float *LSE;
@@ -195,12 +195,13 @@ __device__ __forceinline__ void load_vec(const float *src, int rows, int row0, f
                                              (int)((uint32_t)row0 * 4u), 0, 0);
 }
 
-// C (32 rows x 32 columns) += A B over the head dim: A rows from LDS at
-// `base` (row read offsets), B operand resident in registers.
+// C (32 rows x 32 columns) = init + A B over the head dim: A rows from LDS
+// at `base` (row read offsets), B operand resident in registers.
 template <int D>
-__device__ __forceinline__ f32x16 rows_times(const char *base, const Offsets<D> &off, const bf16x8 *bop)
+__device__ __forceinline__ f32x16 rows_times(const char *base, const Offsets<D> &off, const bf16x8 *bop,
+                                             const f32x16 &init = f32x16{})
 {
-    f32x16 c = {};
+    f32x16 c = init;
 #pragma unroll
     for (int st = 0; st < Shape<D>::kSteps; ++st)
         c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*LDS_PTR(const bf16x8, base + off.row[st]), bop[st], c, 0, 0, 0);
@@ -355,7 +356,7 @@ __global__ __launch_bounds__(Shape<D>::kThreads) __attribute__((amdgpu_waves_per
         const float l2 = q_ok ? a.LSE[(size_t)bh * N + qidx] * kLog2e : 0.f;
         if (q_ok && half == 0) {
             a.L2[(size_t)bh * N + qidx] = l2;
-            a.Dsum[(size_t)bh * N + qidx] = dsum;
+            a.Dsum[(size_t)bh * N + qidx] = -dsum;  // negated: the dK/dV kernel's dP starts from it
         }
 
         f32x16 dq[S::kDBlocks];
@@ -536,11 +537,21 @@ __global__ __launch_bounds__(Shape<D>::kThreads) __attribute__((amdgpu_waves_per
                     continue;
                 const char *qbase = qc + qb * kRows * S::kRowBytes;
                 const char *gbase = gc + qb * kRows * S::kRowBytes;
-                const f32x16 s = rows_times<D>(qbase, off, kop);
-                const f32x16 dp = rows_times<D>(gbase, off, vop);
-                // Register 4 j + e holds query qs0 + 8 j + 4 half + e.  Queries
+                // Register 4 j + e holds query qs0 + 8 j + 4 half + e.  The dP
+                // product starts from -D of those queries (the workspace holds
+                // -D), so it yields dP - D with no VALU subtraction.  Queries
                 // past N have zero Q and dO rows and L2 = D = 0: p = 1 there,
                 // but both products it feeds multiply a zero row.
+                f32x16 neg_d;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const f32x4 d4 = *LDS_PTR(const f32x4, dc + qb * kRows + 8 * j + 4 * half);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        neg_d[4 * j + e] = d4[e];
+                }
+                const f32x16 s = rows_times<D>(qbase, off, kop);
+                const f32x16 dpd = rows_times<D>(gbase, off, vop, neg_d);
                 const bool masked = CAUSAL && qs0 < kw0 + kRows - 1;
                 // Query qs0 + 8 j + 4 half + e is masked iff 8 j + e < thr.
                 const int thr = masked ? kidx - qs0 - 4 * half : 0;
@@ -549,14 +560,13 @@ __global__ __launch_bounds__(Shape<D>::kThreads) __attribute__((amdgpu_waves_per
                 for (int j = 0; j < 4; ++j) {
                     const int qr = qb * kRows + 8 * j + 4 * half;
                     const f32x4 l4 = *LDS_PTR(const f32x4, lc + qr);
-                    const f32x4 d4 = *LDS_PTR(const f32x4, dc + qr);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int r = 4 * j + e;
                         float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.c_log2, -l4[e]));
                         pr = (8 * j + e < thr) ? 0.f : pr;
                         p[r] = pr;
-                        ds[r] = pr * (dp[r] - d4[e]);
+                        ds[r] = pr * dpd[r];
                     }
                 }
                 bf16x8 pb[2], dsb[2];
