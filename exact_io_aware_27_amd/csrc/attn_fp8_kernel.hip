@@ -122,12 +122,12 @@ __device__ __forceinline__ float row_butterfly(float v, float sign)
 // columns 8 (t % 16) .. +7 of four rows: rows 16 p + t / 16 (p = 0..3), or,
 // for the transposed V, the consecutive rows 4 (t / 16) + p.  ROTATE applies
 // the signs and the fast Hadamard transform (three stages inside a thread,
-// four across the 16 lanes of a row, through DPP moves), then every value is
-// multiplied by `mul` in fp32 (1 leaves it as it is; Q takes the softmax
-// scale in log2 units); TRANSPOSE converts
+// four across the 16 lanes of a row, through DPP moves); SCALE then
+// multiplies every value by `mul` in fp32 (Q's softmax scale in log2 units);
+// TRANSPOSE converts
 // column by column (the four rows of one column are four consecutive bytes of
 // the tile's key order) and writes V^T through LDS.
-template <bool ROTATE, bool TRANSPOSE>
+template <bool ROTATE, bool TRANSPOSE, bool SCALE>
 __global__ __launch_bounds__(256) void quantize_kernel(const __bf16 *__restrict__ x, uint8_t *__restrict__ out,
                                                        uint8_t *__restrict__ exps, int N, int Np, int nblk,
                                                        uint32_t s0, uint32_t s1, uint32_t s2, uint32_t s3, float mul)
@@ -180,7 +180,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(const __bf16 *__restrict_
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            v[p][e] *= mul;
+            if constexpr (SCALE)
+                v[p][e] *= mul;
             amax = fmaxf(amax, fabsf(v[p][e]));
         }
     }
@@ -685,15 +686,23 @@ hipError_t attn_fp8_quantize_launch(const AttnFp8Quantize &q)
     const uint32_t s0 = s ? s[0] : 0, s1 = s ? s[1] : 0, s2 = s ? s[2] : 0, s3 = s ? s[3] : 0;
     const __bf16 *x = (const __bf16 *)q.x;
     uint8_t *out = (uint8_t *)q.out, *exps = (uint8_t *)q.exps;
+    // (a multiplier of exactly 1 is skipped: the product would change nothing)
+    const bool scale = q.mul != 1.f;
     if (q.transpose)
-        hipLaunchKernelGGL((quantize_kernel<false, true>), dim3(grid), dim3(256), 0, q.stream, x, out, exps, (int)q.N, Np,
-                           nblk, 0u, 0u, 0u, 0u, 1.f);
+        hipLaunchKernelGGL((quantize_kernel<false, true, false>), dim3(grid), dim3(256), 0, q.stream, x, out, exps,
+                           (int)q.N, Np, nblk, 0u, 0u, 0u, 0u, 1.f);
+    else if (s && scale)
+        hipLaunchKernelGGL((quantize_kernel<true, false, true>), dim3(grid), dim3(256), 0, q.stream, x, out, exps,
+                           (int)q.N, Np, nblk, s0, s1, s2, s3, q.mul);
     else if (s)
-        hipLaunchKernelGGL((quantize_kernel<true, false>), dim3(grid), dim3(256), 0, q.stream, x, out, exps, (int)q.N, Np,
-                           nblk, s0, s1, s2, s3, q.mul);
+        hipLaunchKernelGGL((quantize_kernel<true, false, false>), dim3(grid), dim3(256), 0, q.stream, x, out, exps,
+                           (int)q.N, Np, nblk, s0, s1, s2, s3, 1.f);
+    else if (scale)
+        hipLaunchKernelGGL((quantize_kernel<false, false, true>), dim3(grid), dim3(256), 0, q.stream, x, out, exps,
+                           (int)q.N, Np, nblk, 0u, 0u, 0u, 0u, q.mul);
     else
-        hipLaunchKernelGGL((quantize_kernel<false, false>), dim3(grid), dim3(256), 0, q.stream, x, out, exps, (int)q.N, Np,
-                           nblk, 0u, 0u, 0u, 0u, q.mul);
+        hipLaunchKernelGGL((quantize_kernel<false, false, false>), dim3(grid), dim3(256), 0, q.stream, x, out, exps,
+                           (int)q.N, Np, nblk, 0u, 0u, 0u, 0u, 1.f);
     return hipGetLastError();
 }
 
