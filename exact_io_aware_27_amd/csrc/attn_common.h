@@ -59,6 +59,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));  // RNE
 }
 
+// Position pos of `count` dispatch positions of one XCD -> the work rank it
+// takes.  The XCD deals its positions to its 32 CUs in rounds of 32; odd
+// rounds run backwards (the last round over its own length), so a CU that
+// takes a heavy rank in one round takes a light one in the next.  A
+// permutation of [0, count).
+constexpr int kCusPerXcd = 32;  // MI355X: 256 CUs over 8 XCDs
+__device__ __forceinline__ int snake_slot(int pos, int count)
+{
+    const int round = pos / kCusPerXcd, i = pos % kCusPerXcd;
+    const int len = min(kCusPerXcd, count - round * kCusPerXcd);
+    return (round & 1) ? round * kCusPerXcd + (len - 1 - i) : pos;
+}
+
 // Logical workgroup order: XCD-major (consecutive logical indices share an
 // XCD, so the units of one head stay on one XCD), then head-major.
 __device__ __forceinline__ void unit_of(int wg, int n_wg, int n_units, int &bh, int &unit)

@@ -250,12 +250,17 @@ __global__ __launch_bounds__((Tile<D, W>::kThreads)) __attribute__((
     // within each XCD: XCD x owns heads [x B H / 8, (x + 1) B H / 8), and its
     // workgroups walk them tile by tile from the heaviest (the host chooses
     // this only when 8 divides B H).  Uneven work then fills the slots the
-    // pairs would have left idle.
+    // pairs would have left idle.  The XCD's dispatch positions are dealt to
+    // its CUs in rounds, so the rounds alternate direction (snake_slot): the
+    // CU that takes the heaviest tile of one round takes the lightest of the
+    // next, which evens out the work each CU holds (gpt2_small +3.4%,
+    // bitwise-equal output).
     const bool lpt = CAUSAL && !SPLIT && a.lpt;
     const int n_units = (CAUSAL && !lpt) ? (nqt + 1) / 2 : nqt;
     int bh, rem;
     if (lpt) {
-        const int hpx = a.BH / kXcds, xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+        const int hpx = a.BH / kXcds, xcd = blockIdx.x % kXcds;
+        const int slot = snake_slot(blockIdx.x / kXcds, hpx * nqt);
         bh = xcd * hpx + slot % hpx;
         rem = (nqt - 1) - slot / hpx;
     } else {
