@@ -529,9 +529,11 @@ def bench_fp8(args):
 def bench_micro(args):
     """One JSON line of gfx950 issue rates (exact_io_aware_27_amd/micro.py):
     cycles per VALU instruction by kind and waves per SIMD, dependent-chain
-    latencies, and cycles per 32x32x16 bf16 MFMA when k FMAs and e
-    exponentials follow each one -- the per-unit cycle count the attention
-    kernels are designed against, measured in shader cycles."""
+    latencies, cycles per 32x32x16 bf16 MFMA when k FMAs and e
+    exponentials follow each one, LDS read throughput, and cycles per MFMA
+    when its operand comes from LDS in the attention step's issue order --
+    the per-unit cycle count the attention kernels are designed against,
+    measured in shader cycles."""
     import torch
 
     from exact_io_aware_27_amd import micro
@@ -564,8 +566,23 @@ def bench_micro(args):
                   % (k, e, m["shape"], w, m["cycles_per_mfma"], m["tflops"], m["clock_ghz"]),
                   file=sys.stderr, flush=True)
             mixes.append(m)
+    lds_rates = []
+    for kind in (0, 1):
+        for w in (1, 2, 4):
+            r = micro.lds_rate(kind, w)
+            print("lds %-18s waves/SIMD %d: %.1f bytes/cycle per CU  (%.2f GHz)"
+                  % (r["read"], w, r["bytes_per_cycle_per_cu"], r["clock_ghz"]), file=sys.stderr, flush=True)
+            lds_rates.append(r)
+    lds_mixes = []
+    for kind in (0, 1, 2):
+        for w in (1, 2):
+            m = micro.mix_lds(kind, w)
+            print("MFMA with its operand from LDS (%s), waves/SIMD %d: %.2f cycles/MFMA, %.0f TFLOP/s (%.2f GHz)"
+                  % (m["operand"], w, m["cycles_per_mfma"], m["tflops"], m["clock_ghz"]), file=sys.stderr,
+                  flush=True)
+            lds_mixes.append(m)
     out = {"metric": "gfx950 issue rates (shader cycles), 1 GPU", "unit": "cycles", "rates": rates,
-           "mixes": mixes, "note": "rate: per SIMD over all its waves (independent chains) or per dependent "
+           "mixes": mixes, "lds_rates": lds_rates, "lds_mixes": lds_mixes, "note": "rate: per SIMD over all its waves (independent chains) or per dependent "
                                   "instruction; mix: per 32x32x16 bf16 MFMA per SIMD (32 = matrix-core rate)"}
     print(json.dumps(out), flush=True)
     return 0

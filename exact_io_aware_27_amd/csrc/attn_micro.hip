@@ -17,6 +17,10 @@
 //          followed by k FMAs and e exponentials (v_exp_f32, or exp2_poly)
 //          on independent chains, interleaved by sched_group_barrier as the
 //          attention kernel interleaves its step: cycles per MFMA per SIMD.
+//   lds:   LDS read throughput (ds_read_b128, ds_read_b64_tr_b16): bytes
+//          per cycle per CU.
+//   mix_lds: MFMAs whose streamed operand is read from LDS in the step's
+//          issue order, with no VALU: cycles per MFMA per SIMD.
 //
 // Occupancy is pinned: one workgroup per CU (96 KB of LDS each) of 4 w waves,
 // so every SIMD holds exactly w waves.  256 workgroups fill the 256 CUs.
@@ -178,6 +182,132 @@ __global__ __launch_bounds__(1024) void mix_kernel(float *sink, unsigned long lo
     sink[(size_t)blockIdx.x * blockDim.x + t] = s + (float)lds_pin[t & 7];
 }
 
+// LDS contents for the LDS kernels: small bf16 values (defined data, and
+// MFMA inputs that toggle like real operands).
+__device__ __forceinline__ void lds_fill(char *lds)
+{
+    for (int i = threadIdx.x; i < kLdsBytes / 16; i += blockDim.x) {
+        const uint32_t w = 0x3c003c00u + ((uint32_t)(i * 2654435761u) & 0x00ff00ffu);
+        *LDS_PTR(u32x4, lds + 16 * i) = u32x4{w, w ^ 0x00110011u, w ^ 0x00220022u, w ^ 0x00330033u};
+    }
+}
+
+// One wave-wide LDS read of an MFMA A operand (8 bf16 a lane, 1 KB a wave):
+// KIND 0 one ds_read_b128 (the K operand of the score product), KIND 1 two
+// ds_read_b64_tr_b16 (the V^T operand of P V).  Lanes read consecutive
+// addresses: no bank conflicts.
+template <int KIND>
+__device__ __forceinline__ bf16x8 lds_operand(const char *lds, uint32_t off, int j)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    if constexpr (KIND == 0) {
+        return *LDS_PTR(const bf16x8, lds + off + 16 * lane + 1024 * j);
+    } else {
+        const u32x2 lo = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, lds + off + 8 * lane + 1024 * j)));
+        const u32x2 hi = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, lds + off + 8 * lane + 1024 * j + 512)));
+        const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+        return __builtin_bit_cast(bf16x8, w);
+    }
+}
+
+// LDS read throughput: each wave issues 16 independent reads per iteration
+// (KIND 0: ds_read_b128, 16 bytes a lane; KIND 1: ds_read_b64_tr_b16, 8
+// bytes a lane) and waits for them; w waves per SIMD overlap their batches.
+// Addresses stay below 16.5 KB of the 96 KB allocation.
+template <int KIND>
+__global__ __launch_bounds__(1024) void lds_rate_kernel(float *sink, unsigned long long *times, int iters)
+{
+    extern __shared__ char lds[];
+    lds_fill(lds);
+    __syncthreads();
+    const int lane = threadIdx.x & (kWave - 1);
+    uint32_t off = 0;
+    uint32_t acc = 0;
+    const uint64_t c0 = __builtin_amdgcn_s_memtime();
+    const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+    for (int it = 0; it < iters; ++it) {
+        asm volatile("" : "+v"(off));  // a fresh address each iteration: no read is hoisted
+        if constexpr (KIND == 0) {
+            u32x4 x[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                x[j] = *LDS_PTR(const u32x4, lds + off + 16 * lane + 1024 * j);
+            asm volatile("" ::"v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]),
+                         "v"(x[7]), "v"(x[8]), "v"(x[9]), "v"(x[10]), "v"(x[11]), "v"(x[12]), "v"(x[13]),
+                         "v"(x[14]), "v"(x[15]));
+            acc ^= x[0][0] ^ x[15][3];
+        } else {
+            s16x4 x[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                x[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, lds + off + 8 * lane + 512 * j));
+            asm volatile("" ::"v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]),
+                         "v"(x[7]), "v"(x[8]), "v"(x[9]), "v"(x[10]), "v"(x[11]), "v"(x[12]), "v"(x[13]),
+                         "v"(x[14]), "v"(x[15]));
+            acc ^= (uint32_t)(uint16_t)(x[0][0] ^ x[15][3]);
+        }
+    }
+    record(times, c0, r0);
+    sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = (float)(acc & 0xff);
+}
+
+// The attention step's matrix-core and LDS work without its softmax: 16
+// MFMAs per iteration on four accumulators, the A operand of each (1 KB a
+// wave) read from LDS inside the iteration: KIND 0 one ds_read_b128 each,
+// KIND 1 two ds_read_b64_tr_b16 each, KIND 2 the step's mix (ds_read_b128
+// for the first 8 MFMAs, as the score product reads K; the transposing pair
+// for the last 8, as P V reads V^T).  The issue order is the step's: 4 reads
+// up front, then per MFMA the MFMA and up to 2 reads for the MFMAs ahead.
+// One or two waves per SIMD (the attention kernels run two), with the
+// register budget of two stated: without it the scheduler keeps source
+// order, each read right before its MFMA, to protect an occupancy the launch
+// never uses.
+template <int KIND>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void mix_lds_kernel(
+    float *sink, unsigned long long *times, int iters)
+{
+    extern __shared__ char lds[];
+    const int t = threadIdx.x;
+    lds_fill(lds);
+    __syncthreads();
+    bf16x8 b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        b[i] = (__bf16)(0.002f * (float)((t + 3 * i) & 63));
+    f32x16 acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        acc[j] = f32x16{};
+    uint32_t off = 0;
+    const uint64_t c0 = __builtin_amdgcn_s_memtime();
+    const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+    for (int it = 0; it < iters; ++it) {
+        asm volatile("" : "+v"(off));  // a fresh address each iteration: no read is hoisted
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const bf16x8 a = (KIND == 0 || (KIND == 2 && i < 8)) ? lds_operand<0>(lds, off, i)
+                                                                  : lds_operand<KIND == 0 ? 0 : 1>(lds, off, i);
+            acc[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i & 3], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS read
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+        }
+    }
+    record(times, c0, r0);
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            s += acc[j][i];
+    sink[(size_t)blockIdx.x * blockDim.x + t] = s;
+}
+
 template <typename F>
 static int run(F kernel, int waves_per_simd, int iters, double *cycles, double *clock_ghz, double *ms)
 {
@@ -336,6 +466,55 @@ extern "C" __attribute__((visibility("default"))) int attn_micro_mix_shape(int k
     if (st != 0)
         return st;
     const double mfmas = (double)iters * 4;
+    out[0] = cyc / (mfmas * waves_per_simd);
+    out[1] = ghz;
+    out[2] = ms;
+    out[3] = 256.0 * 4 * waves_per_simd * mfmas * 32768.0 / (ms * 1e-3) / 1e12;
+    return 0;
+}
+
+// LDS read throughput: kind 0 ds_read_b128, 1 ds_read_b64_tr_b16; waves per
+// SIMD 1..4.  out[0] = bytes read per shader cycle per CU (all its waves),
+// out[1] = shader clock (GHz), out[2] = ms.  Returns 0, 2 for arguments
+// outside the table, 7 for a HIP error.
+extern "C" __attribute__((visibility("default"))) int attn_micro_lds_rate(int kind, int waves_per_simd, int iters,
+                                                                          double *out)
+{
+    double cyc = 0, ghz = 0, ms = 0;
+    int st = 2;
+    if (kind == 0)
+        st = run(lds_rate_kernel<0>, waves_per_simd, iters, &cyc, &ghz, &ms);
+    else if (kind == 1)
+        st = run(lds_rate_kernel<1>, waves_per_simd, iters, &cyc, &ghz, &ms);
+    if (st != 0)
+        return st;
+    const double bytes = (double)iters * 16 * (kind == 0 ? 1024 : 512) * 4 * waves_per_simd;
+    out[0] = bytes / cyc;
+    out[1] = ghz;
+    out[2] = ms;
+    return 0;
+}
+
+// MFMAs fed from LDS: each 32x32x16 bf16 MFMA's A operand (1 KB a wave)
+// read from LDS (kind 0 ds_read_b128, 1 two ds_read_b64_tr_b16, 2 the two as
+// the attention step mixes them); one or two waves per SIMD.  out as
+// attn_micro_mix.
+extern "C" __attribute__((visibility("default"))) int attn_micro_mix_lds(int kind, int waves_per_simd, int iters,
+                                                                         double *out)
+{
+    double cyc = 0, ghz = 0, ms = 0;
+    int st = 2;
+    if (waves_per_simd > 2)
+        return 2;
+    if (kind == 0)
+        st = run(mix_lds_kernel<0>, waves_per_simd, iters, &cyc, &ghz, &ms);
+    else if (kind == 1)
+        st = run(mix_lds_kernel<1>, waves_per_simd, iters, &cyc, &ghz, &ms);
+    else if (kind == 2)
+        st = run(mix_lds_kernel<2>, waves_per_simd, iters, &cyc, &ghz, &ms);
+    if (st != 0)
+        return st;
+    const double mfmas = (double)iters * 16;
     out[0] = cyc / (mfmas * waves_per_simd);
     out[1] = ghz;
     out[2] = ms;

@@ -33,6 +33,10 @@ def load():
     lib.attn_micro_mix.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, d4]
     lib.attn_micro_mix_shape.restype = ctypes.c_int
     lib.attn_micro_mix_shape.argtypes = [ctypes.c_int] * 6 + [d4]
+    lib.attn_micro_lds_rate.restype = ctypes.c_int
+    lib.attn_micro_lds_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, d4]
+    lib.attn_micro_mix_lds.restype = ctypes.c_int
+    lib.attn_micro_mix_lds.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, d4]
     lib.attn_micro_exp2.restype = ctypes.c_int
     lib.attn_micro_exp2.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
                                     ctypes.c_void_p]
@@ -68,6 +72,35 @@ def mix(k_fma, n_exp, poly, waves_per_simd, iters=20000, shape=0):
     return {"k_fma": k_fma, "n_exp": n_exp, "exp": "exp2_poly" if poly else "v_exp_f32", "shape": SHAPES[shape],
             "waves_per_simd": waves_per_simd, "cycles_per_mfma": out[0], "clock_ghz": out[1],
             "ms": out[2], "tflops": out[3]}
+
+
+LDS_READS = {0: "ds_read_b128", 1: "ds_read_b64_tr_b16"}
+LDS_OPERANDS = {0: "ds_read_b128", 1: "2 x ds_read_b64_tr_b16",
+                2: "ds_read_b128 for 8 MFMAs, 2 x ds_read_b64_tr_b16 for 8 (the attention step)"}
+
+
+def lds_rate(kind, waves_per_simd, iters=20000):
+    """LDS read throughput of one read kind (0 ds_read_b128, 1
+    ds_read_b64_tr_b16) on consecutive addresses: bytes per shader cycle per
+    CU over all its waves, and the shader clock (GHz)."""
+    out = (ctypes.c_double * 4)()
+    st = load().attn_micro_lds_rate(kind, waves_per_simd, iters, out)
+    if st:
+        raise RuntimeError("attn_micro_lds_rate status %d" % st)
+    return {"read": LDS_READS[kind], "waves_per_simd": waves_per_simd, "bytes_per_cycle_per_cu": out[0],
+            "clock_ghz": out[1], "ms": out[2]}
+
+
+def mix_lds(kind, waves_per_simd, iters=20000):
+    """Cycles per 32x32x16 bf16 MFMA per SIMD when each MFMA's A operand (1 KB
+    a wave) is read from LDS in the attention step's issue order (kind as
+    LDS_OPERANDS), with no VALU work; one or two waves per SIMD."""
+    out = (ctypes.c_double * 4)()
+    st = load().attn_micro_mix_lds(kind, waves_per_simd, iters, out)
+    if st:
+        raise RuntimeError("attn_micro_mix_lds status %d" % st)
+    return {"operand": LDS_OPERANDS[kind], "waves_per_simd": waves_per_simd, "cycles_per_mfma": out[0],
+            "clock_ghz": out[1], "ms": out[2], "tflops": out[3]}
 
 
 def exp2(x, stream=None):
