@@ -612,6 +612,8 @@ def main():
                     help="gfx950 issue-rate microbenchmarks (VALU, exp, exp2_poly, MFMA mixes) in shader cycles")
     ap.add_argument("--cpu-heads", type=int, default=1,
                     help="--bwd: whole heads in the oracle's CPU-baseline sample (0: skip)")
+    ap.add_argument("--per-launch", action="store_true",
+                    help="add each timed launch's duration, in launch order, as ms_launches")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (HBM counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -701,7 +703,8 @@ def main():
         events[i + 1].record(stream)
     torch.cuda.synchronize()
     ms = events[0].elapsed_time(events[-1]) / args.steps  # one kernel per step: average launch duration
-    per_launch = sorted(events[i].elapsed_time(events[i + 1]) for i in range(args.steps))
+    in_order = [events[i].elapsed_time(events[i + 1]) for i in range(args.steps)]
+    per_launch = sorted(in_order)
     ms_median = per_launch[len(per_launch) // 2] if len(per_launch) % 2 else \
         0.5 * (per_launch[len(per_launch) // 2 - 1] + per_launch[len(per_launch) // 2])
 
@@ -722,6 +725,7 @@ def main():
         "ms_median": round(ms_median, 5),
         "ms_min": round(per_launch[0], 5),
         "ms_max": round(per_launch[-1], 5),
+        **({"ms_launches": [round(x, 5) for x in in_order]} if args.per_launch else {}),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
