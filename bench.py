@@ -581,8 +581,16 @@ def bench_micro(args):
                   % (m["operand"], w, m["cycles_per_mfma"], m["tflops"], m["clock_ghz"]), file=sys.stderr,
                   flush=True)
             lds_mixes.append(m)
+    hbm = []
+    for blocked in (False, True):
+        for wgs in (512, 1024, 2048, 4096, 8192):
+            h = micro.hbm_read(4096, wgs, blocked)
+            print("hbm read stream, 4 GiB, %d workgroups of 256, %s: %.0f GB/s"
+                  % (wgs, "one slice per workgroup" if blocked else "grid-interleaved", h["GBps"]),
+                  file=sys.stderr, flush=True)
+            hbm.append(h)
     out = {"metric": "gfx950 issue rates (shader cycles), 1 GPU", "unit": "cycles", "rates": rates,
-           "mixes": mixes, "lds_rates": lds_rates, "lds_mixes": lds_mixes, "note": "rate: per SIMD over all its waves (independent chains) or per dependent "
+           "mixes": mixes, "lds_rates": lds_rates, "lds_mixes": lds_mixes, "hbm_read": hbm, "note": "rate: per SIMD over all its waves (independent chains) or per dependent "
                                   "instruction; mix: per 32x32x16 bf16 MFMA per SIMD (32 = matrix-core rate)"}
     print(json.dumps(out), flush=True)
     return 0

@@ -21,6 +21,8 @@
 //          per cycle per CU.
 //   mix_lds: MFMAs whose streamed operand is read from LDS in the step's
 //          issue order, with no VALU: cycles per MFMA per SIMD.
+//   hbm:   a plain read stream over a large buffer: GB/s, the ceiling of a
+//          bandwidth-bound kernel's reads.
 //
 // Occupancy is pinned: one workgroup per CU (96 KB of LDS each) of 4 w waves,
 // so every SIMD holds exactly w waves.  256 workgroups fill the 256 CUs.
@@ -308,6 +310,38 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     sink[(size_t)blockIdx.x * blockDim.x + t] = s;
 }
 
+// HBM read stream: every thread reads 16-byte words of a large buffer in a
+// grid-stride loop, four loads in flight per iteration, and folds them into
+// one word (written once, so the loads are not removed).  The ceiling a
+// bandwidth-bound kernel of this chip can reach on reads alone.
+// BLOCKED: each workgroup streams its own contiguous slice of the buffer,
+// 16 KB per iteration (as a K/V stream walks one head), instead of the
+// grid-wide interleave.
+template <bool BLOCKED>
+__global__ __launch_bounds__(256) void hbm_read_kernel(const u32x4 *__restrict__ src, size_t n16,
+                                                       uint32_t *__restrict__ sink)
+{
+    size_t i, end, stride;
+    if constexpr (BLOCKED) {
+        const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
+        i = (size_t)blockIdx.x * per + threadIdx.x;
+        end = min(n16, (size_t)(blockIdx.x + 1) * per);
+        stride = blockDim.x;
+    } else {
+        i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+        end = n16;
+        stride = (size_t)gridDim.x * blockDim.x;
+    }
+    u32x4 acc = {};
+    for (; i + 3 * stride < end; i += 4 * stride) {
+        const u32x4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+        acc ^= a ^ b ^ c ^ d;
+    }
+    for (; i < end; i += stride)
+        acc ^= src[i];
+    sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
 template <typename F>
 static int run(F kernel, int waves_per_simd, int iters, double *cycles, double *clock_ghz, double *ms)
 {
@@ -520,6 +554,55 @@ extern "C" __attribute__((visibility("default"))) int attn_micro_mix_lds(int kin
     out[2] = ms;
     out[3] = 256.0 * 4 * waves_per_simd * mfmas * 32768.0 / (ms * 1e-3) / 1e12;
     return 0;
+}
+
+// HBM read bandwidth: `mib` MiB (at least 64) read by hbm_read_kernel on
+// `wgs` workgroups of 256 threads (256..65536), grid-interleaved or
+// (blocked != 0) one contiguous slice per workgroup, the last of `reps`
+// launches (1..100) timed with HIP events.  out[0] = GB/s, out[1] = ms.
+// Returns 0, 2 for arguments outside those ranges, 7 for a HIP error
+// (allocation included).
+extern "C" __attribute__((visibility("default"))) int attn_micro_hbm_read(int mib, int wgs, int reps, int blocked,
+                                                                          double *out)
+{
+    if (mib < 64 || wgs < 256 || wgs > 65536 || reps < 1 || reps > 100)
+        return 2;
+    const size_t bytes = (size_t)mib << 20;
+    void *src = nullptr;
+    uint32_t *sink = nullptr;
+    if (hipMalloc(&src, bytes) != hipSuccess)
+        return 7;
+    if (hipMalloc(&sink, (size_t)wgs * 256 * sizeof(uint32_t)) != hipSuccess) {
+        (void)hipFree(src);
+        return 7;
+    }
+    int status = hipMemset(src, 0x5a, bytes) == hipSuccess ? 0 : 7;
+    hipEvent_t e0, e1;
+    (void)hipEventCreate(&e0);
+    (void)hipEventCreate(&e1);
+    float ms = 0.f;
+    for (int r = 0; r < reps && status == 0; ++r) {
+        (void)hipEventRecord(e0, nullptr);
+        if (blocked)
+            hipLaunchKernelGGL(hbm_read_kernel<true>, dim3(wgs), dim3(256), 0, nullptr,
+                               (const attn_gfx950::u32x4 *)src, bytes / 16, sink);
+        else
+            hipLaunchKernelGGL(hbm_read_kernel<false>, dim3(wgs), dim3(256), 0, nullptr,
+                               (const attn_gfx950::u32x4 *)src, bytes / 16, sink);
+        (void)hipEventRecord(e1, nullptr);
+        if (hipGetLastError() != hipSuccess || hipEventSynchronize(e1) != hipSuccess)
+            status = 7;
+    }
+    if (status == 0) {
+        (void)hipEventElapsedTime(&ms, e0, e1);
+        out[0] = (double)bytes / (ms * 1e-3) / 1e9;
+        out[1] = ms;
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    (void)hipFree(src);
+    (void)hipFree(sink);
+    return status;
 }
 
 // poly[i] = exp2_poly(x[i]) and hw[i] = v_exp_f32(x[i]) for i < n; x, poly

@@ -37,6 +37,8 @@ def load():
     lib.attn_micro_lds_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, d4]
     lib.attn_micro_mix_lds.restype = ctypes.c_int
     lib.attn_micro_mix_lds.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, d4]
+    lib.attn_micro_hbm_read.restype = ctypes.c_int
+    lib.attn_micro_hbm_read.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, d4]
     lib.attn_micro_exp2.restype = ctypes.c_int
     lib.attn_micro_exp2.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
                                     ctypes.c_void_p]
@@ -101,6 +103,17 @@ def mix_lds(kind, waves_per_simd, iters=20000):
         raise RuntimeError("attn_micro_mix_lds status %d" % st)
     return {"operand": LDS_OPERANDS[kind], "waves_per_simd": waves_per_simd, "cycles_per_mfma": out[0],
             "clock_ghz": out[1], "ms": out[2], "tflops": out[3]}
+
+
+def hbm_read(mib, wgs, blocked=False, reps=10):
+    """GB/s of a plain 16-byte-per-thread read stream over `mib` MiB on
+    `wgs` workgroups of 256 threads, grid-interleaved or (blocked) one
+    contiguous slice per workgroup (the last of `reps` launches)."""
+    out = (ctypes.c_double * 4)()
+    st = load().attn_micro_hbm_read(mib, wgs, reps, 1 if blocked else 0, out)
+    if st:
+        raise RuntimeError("attn_micro_hbm_read status %d" % st)
+    return {"mib": mib, "workgroups": wgs, "blocked": blocked, "GBps": out[0], "ms": out[1]}
 
 
 def exp2(x, stream=None):
